@@ -1,0 +1,80 @@
+"""Dequantised-weight definitions (oracle; test infrastructure only).
+
+These are the bit-exact targets of the library's debug decoders.
+"""
+import numpy as np
+from .codecs import e4m3_to_f64, e2m1_to_f64, f16_bits_to_f64, f64_to_f16_bits
+from .pack import block64_unpack, awq_unpack_bank
+
+
+def fp8w_dequant(w, scale):
+    """FP8 E4M3 per-output-channel weights -> float32.
+
+    dq[n, k] = F8E4M3ToF32(w[n, k]) * scale[n]  (issue "tp>1 fp8w tail-MLP
+    shard ...", sections "Mechanism on the tp>1 path" and "Logic anchor").
+    w: uint8 [N, K]; scale: float32 [N].  The float64 product of a 4-bit and a
+    24-bit significand is exact, so one rounding to float32 reproduces the
+    float32 multiply.
+    """
+    s = np.asarray(scale, dtype=np.float32).astype(np.float64)
+    return (e4m3_to_f64(w) * s[:, None]).astype(np.float32)
+
+
+def nvfp4_inv_global(global_scale):
+    """The runtime dequantisation factor 1/weight_global_scale, rounded once to float32
+    (page "Qwen3.8-27B-NVFP4", section "NVFP4 numerics as implemented")."""
+    return np.float32(1.0 / np.float64(np.float32(global_scale)))
+
+
+def nvfp4_dequant_parts(weight_packed, weight_scale, global_scale):
+    """Three-level NVFP4 tensor -> float32, from the checkpoint tensors.
+
+    weight_packed: uint8 [N, K/2], two E2M1 per byte, low nibble = earlier weight;
+    weight_scale: uint8 E4M3 [N, K/16], one per 16 consecutive input channels;
+    global_scale: float32, applied as 1/global_scale (page "Qwen3.8-27B-NVFP4",
+    section "NVFP4 numerics as implemented").
+    dq = RN_f32(e2m1(q) * e4m3(d) * RN_f32(1/gs)); the float64 product is exact.
+    """
+    wp = np.asarray(weight_packed, dtype=np.uint8)
+    n, khalf = wp.shape
+    k = khalf * 2
+    nib = np.empty((n, k), dtype=np.uint8)
+    nib[:, 0::2] = wp & 0x0F
+    nib[:, 1::2] = wp >> 4
+    d = e4m3_to_f64(np.asarray(weight_scale, dtype=np.uint8))          # [N, K/16]
+    dk = np.repeat(d, 16, axis=1)                                       # [N, K]
+    inv = np.float64(nvfp4_inv_global(global_scale))
+    return (e2m1_to_f64(nib) * dk * inv).astype(np.float32)
+
+
+def nvfp4_dequant(blk, global_scale):
+    """Block64 records [N, K/64, 36] -> float32 [N, K] (same definition as above)."""
+    wp, ws = block64_unpack(blk)
+    return nvfp4_dequant_parts(wp, ws, global_scale)
+
+
+def awq_dequant_parts(codes, scales_bits, zeros):
+    """AWQ int4 group-32 -> float16 bits.
+
+    dq = RN_f16(q * s + RN_f16(-z * s)): one fused multiply-add in half
+    precision with the bias -z*s rounded to half first (page "[Kernel][SM70]
+    Add native-g32 AWQ QPN M1 operator", section "What it does": the
+    half_fma(q, scale, half(-zero*scale)) boundary, not half((q-zero)*scale)).
+    codes: uint8 [..., N, K] in 0..15; scales_bits: uint16 (f16 bits) [..., N, K/32];
+    zeros: uint8 [..., N, K/32].  Returns uint16 f16 bits [..., N, K].
+    The float64 expression is exact (spans < 53 bits), so casting to float16
+    applies the single rounding of the fused operation.
+    """
+    q = np.asarray(codes).astype(np.float64)
+    s = f16_bits_to_f64(scales_bits)
+    z = np.asarray(zeros).astype(np.float64)
+    bias = f16_bits_to_f64(f64_to_f16_bits(-z * s))
+    sk = np.repeat(s, 32, axis=-1)
+    bk = np.repeat(bias, 32, axis=-1)
+    return f64_to_f16_bits(q * sk + bk)
+
+
+def awq_dequant(bank, E, N, K, meta_layout=3):
+    """Prepared bank -> f16 bits [E, N, K] (unpacks the documented bank layout)."""
+    codes, scales, zeros = awq_unpack_bank(bank, E, N, K, meta_layout)
+    return awq_dequant_parts(codes, scales, zeros)
