@@ -1,0 +1,218 @@
+/*
+ * wqmlp.h -- C ABI of the weight-only-quantized SwiGLU MLP library for MI355X (gfx950).
+ *
+ * The library computes, inside HIP kernels and with the weights left packed in
+ * device memory, the dense SwiGLU MLP
+ *
+ *     act[m,i] = silu(sum_k x[m,k] * dq(gate[i,k])) * (sum_k x[m,k] * dq(up[i,k]))
+ *     out[m,o] = sum_q act[m,q] * dq(down[o,q])
+ *
+ * (issue "tp>1 fp8w tail-MLP shard host-dequantizes every layer", section
+ * "Proposed fix") for FP8 E4M3 per-output-channel and NVFP4 weights, and the
+ * AWQ int4 group-32 routed-expert single-token step (pull request "[Kernel][SM70]
+ * Add native-g32 AWQ QPN M1 operator", section "What it does").
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers on the current HIP device unless stated.
+ *     The caller owns every buffer; the library never allocates, frees or
+ *     synchronises inside these calls (capturable into a hipGraph).
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Work is enqueued on it and the call returns at once.
+ *   - Tensors are dense row-major.  Every pointer must be 16-byte aligned.
+ *   - Return value: WQ_OK or a negative WQ_E* code.  Argument errors are
+ *     detected before anything is enqueued (pure arithmetic checks first,
+ *     then the device/pointer/arch checks).  A failed launch returns
+ *     WQ_ELAUNCH and wq_last_hip_error() gives the hipError_t.  There is no
+ *     fallback path of any kind.
+ *   - M == 0 (no activation rows) is a valid empty call: WQ_OK, nothing enqueued.
+ */
+#ifndef WQMLP_H
+#define WQMLP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define WQ_ABI_VERSION 1
+
+/* activation element types */
+enum { WQ_F32 = 0, WQ_BF16 = 1, WQ_F16 = 2 };
+/* weight formats */
+enum { WQ_FMT_FP8W = 0, WQ_FMT_NVFP4 = 1 };
+/* return codes */
+enum {
+  WQ_OK = 0,
+  WQ_EINVAL = -1,     /* null pointer, bad shape, dtype, format or flags */
+  WQ_EALIGN = -2,     /* a pointer is not 16-byte aligned */
+  WQ_EOVERLAP = -3,   /* an output or the workspace overlaps an input or another output */
+  WQ_EDEVICE = -4,    /* a pointer is not device memory of the current device */
+  WQ_EARCH = -5,      /* the current device is not gfx950 */
+  WQ_EWORKSPACE = -6, /* workspace missing or smaller than the query returns */
+  WQ_ELAUNCH = -7     /* kernel launch failed; see wq_last_hip_error() */
+};
+/* path selection (flags): AUTO picks the MFMA GEMM for M >= WQ_MFMA_MIN_ROWS */
+enum { WQ_PATH_AUTO = 0, WQ_PATH_GEMV = 1, WQ_PATH_MFMA = 2 };
+#define WQ_MFMA_MIN_ROWS 128
+/* largest top-k the routed-expert step accepts */
+#define WQ_MOE_MAX_TOPK 16
+
+/* ABI version of the loaded library (WQ_ABI_VERSION). */
+int wq_abi_version(void);
+/* Static message for a return code. */
+const char* wq_strerror(int rc);
+/* hipError_t of the last WQ_ELAUNCH / WQ_EDEVICE on this host thread (0 if none). */
+int wq_last_hip_error(void);
+
+/*
+ * Workspace (device bytes) that mlp_fp8w_run / mlp_nvfp4_run need for this
+ * shape and path.  fmt: WQ_FMT_*; flags as for the run call.  Returns 0 for
+ * invalid arguments or M == 0.
+ *   GEMV path: act float32 [M, I].
+ *   MFMA path: x as float16 [M, H] (row-scaled), per-row scales float32 [M],
+ *              act float16 [M, I], each region 256-byte aligned.
+ */
+size_t mlp_workspace_bytes(int fmt, int64_t M, int64_t H, int64_t I, int flags);
+
+/*
+ * FP8 E4M3 per-output-channel W8A16 SwiGLU MLP.
+ * Definition: issue "tp>1 fp8w tail-MLP shard ...", sections "Mechanism on the
+ * tp>1 path" (dq[n,k] = F8E4M3ToF32(w[n,k]) * scale[n]) and "Proposed fix"
+ * (the MLP equation, float32 act with no bf16 rounding).
+ *   x       [M, H]  WQ_F32 or WQ_BF16 (x_dtype)
+ *   w_gate  [I, H]  uint8 E4M3fn codes (OCP "fn": bias 7, NaN at 0x7F/0xFF)
+ *   s_gate  [I]     float32 per-output-channel scales;  likewise w_up / s_up
+ *   w_down  [H, I]  uint8 E4M3fn codes;  s_down [H] float32
+ *   out     [M, H]  float32
+ * Shapes: H, I > 0 and multiples of 16 (GEMV) or 64 (MFMA).  Accumulation is
+ * float32; silu(z) = z / (1 + exp(-z)).  The GEMV path (M < 128 under AUTO)
+ * reduces each output over k in a fixed order that does not depend on M, so
+ * results are bitwise reproducible and row m of an M-row call equals a
+ * 1-row call on row m.
+ */
+int mlp_fp8w_run(int64_t M, int64_t H, int64_t I, const void* x, int x_dtype,
+                 const uint8_t* w_gate, const float* s_gate,
+                 const uint8_t* w_up, const float* s_up,
+                 const uint8_t* w_down, const float* s_down,
+                 void* workspace, size_t workspace_bytes, float* out,
+                 int flags, void* stream);
+
+/*
+ * NVFP4 SwiGLU MLP on Block64 records.
+ * Definition: page "Qwen3.8-27B-NVFP4", section "NVFP4 numerics as
+ * implemented": E2M1 weights two per byte (low nibble = earlier weight), one
+ * E4M3 scale per 16 consecutive input channels, and a per-tensor float32
+ * global scale applied as 1/global_scale; the 36-byte record
+ * {uint8 d[4]; uint8 qs[32]} covers 64 consecutive weights of one row, with
+ * d[0..3] the groups in K order.  Records are row-major [rows, cols/64].
+ *   x         [M, H]  WQ_F32 or WQ_BF16
+ *   gate_blk  [I, H/64] records (36 B each); gate_global_scale float32 > 0
+ *   up_blk    [I, H/64] records;             up_global_scale
+ *   down_blk  [H, I/64] records;             down_global_scale
+ *   out       [M, H]  float32
+ * Shapes: H, I > 0 and multiples of 64.  Each K=16 group's partial sum is
+ * scaled by its E4M3 group scale as it completes (GEMV) or the group scale is
+ * folded exactly into the float16 decoded weight (MFMA); 1/global_scale
+ * (rounded once to float32) multiplies the finished dot product.
+ * MFMA path: x rows are scaled by a power of two and rounded to float16, and
+ * act is rounded to float16 before the down GEMM; |act| must stay below
+ * 65504 (larger values overflow to inf and propagate into out).
+ */
+int mlp_nvfp4_run(int64_t M, int64_t H, int64_t I, const void* x, int x_dtype,
+                  const uint8_t* gate_blk, float gate_global_scale,
+                  const uint8_t* up_blk, float up_global_scale,
+                  const uint8_t* down_blk, float down_global_scale,
+                  void* workspace, size_t workspace_bytes, float* out,
+                  int flags, void* stream);
+
+/*
+ * Bytes of a prepared AWQ bank holding E experts of one [N, K] matrix.
+ * Layout (per expert, experts stacked with this per-expert stride / E; every
+ * plane 16-byte aligned):
+ *   codes  [N][K/2] uint8: byte j of row n holds k=2j (low nibble), 2j+1 (high)
+ *   scales [N][K/32] float16
+ *   meta_layout 3: zeros [N][K/32] uint8      (3 bytes of metadata per group)
+ *   meta_layout 4: bias  [N][K/32] float16 = RN_f16(-zero * scale)  (4 bytes)
+ * Returns 0 for invalid arguments.
+ */
+size_t awq_bank_bytes(int64_t E, int64_t N, int64_t K, int meta_layout);
+
+/*
+ * AWQ int4 group-32 routed-expert single-token step.
+ * Definition: pull request "[Kernel][SM70] Add native-g32 AWQ QPN M1
+ * operator", section "What it does":
+ *   dq = RN_f16(fma(q, scale, RN_f16(-zero * scale)))   (not RN_f16((q-zero)*scale))
+ *   for each route r (router order): e = expert_ids[r];
+ *     g = RN_f16(sum_k x[k]*dq13[e][n][k]),  u = RN_f16(sum_k x[k]*dq13[e][n+I][k])
+ *     act[r][n] = RN_f16(silu(g) * u)                                   n < I
+ *     y_r[o] = RN_f16(sum_q act[r][q] * dq2[e][o][q])
+ *   out[o] = RN_f16(sum over valid r, in order, of router_w[r] * y_r[o]) with
+ *   the sum in float32 from 0 (acc = fmaf(w_r, y_r, acc)).
+ *   An id outside [0, E) contributes zero and its act row is zero; duplicate
+ *   valid ids keep their separate router weights.
+ *   x         [H]        float16 bits
+ *   expert_ids[topk]     int32 (device)
+ *   router_w  [topk]     float32 (device)
+ *   w13_bank  E experts of [2I, H] (gate rows 0..I-1, up rows I..2I-1)
+ *   w2_bank   E experts of [H, I]
+ *   act       [topk, I]  float16 out (also the W13 stage's result)
+ *   out       [H]        float16 out
+ * Shapes: E >= 1, 1 <= topk <= WQ_MOE_MAX_TOPK, H and I positive multiples of 32.
+ * Sums are float32; the order inside each dot product is fixed.
+ */
+int moe_awq_m1_run(int64_t E, int64_t topk, int64_t H, int64_t I,
+                   const uint16_t* x, const int32_t* expert_ids, const float* router_w,
+                   const void* w13_bank, const void* w2_bank, int meta_layout,
+                   uint16_t* act, uint16_t* out, void* stream);
+
+/*
+ * Pack checkpoint NVFP4 tensors into Block64 records (one-time, device to device).
+ *   weight_packed [N, K/2] uint8 (low nibble = earlier weight)
+ *   weight_scale  [N, K/16] uint8 E4M3
+ *   blk           [N, K/64, 36] uint8 out: blk[n][b] = weight_scale[n][4b..4b+3] ++ weight_packed[n][32b..32b+31]
+ * K must be a positive multiple of 64 (page "Qwen3.8-27B-NVFP4", section "NVFP4
+ * numerics as implemented": "the host packs these").  16-byte alignment is
+ * not required for this call.
+ */
+int nvfp4_pack_block64(int64_t N, int64_t K, const uint8_t* weight_packed,
+                       const uint8_t* weight_scale, uint8_t* blk, void* stream);
+
+/*
+ * Build a prepared AWQ bank (layout: awq_bank_bytes) from
+ *   codes  [E, N, K] uint8 in 0..15 (one code per byte)
+ *   scales [E, N, K/32] float16 bits
+ *   zeros  [E, N, K/32] uint8
+ * bank must hold awq_bank_bytes(E, N, K, meta_layout) bytes.
+ */
+int awq_pack_bank(int64_t E, int64_t N, int64_t K, const uint8_t* codes,
+                  const uint16_t* scales, const uint8_t* zeros, int meta_layout,
+                  void* bank, void* stream);
+
+/* Debug decoders: the same __device__ decode as the kernels, written out.      */
+/* out[n,k] = RN_f32(e4m3(w[n,k]) * s[n])                              [N, K] f32 */
+int fp8w_dequant_f32(int64_t N, int64_t K, const uint8_t* w, const float* s, float* out, void* stream);
+/* out[n,k] = RN_f32(e2m1(q) * e4m3(d) * RN_f32(1/global_scale))        [N, K] f32 */
+int nvfp4_dequant_f32(int64_t N, int64_t K, const uint8_t* blk, float global_scale, float* out, void* stream);
+/* out[e,n,k] = dq as in moe_awq_m1_run                            [E, N, K] f16 bits */
+int awq_dequant_f16(int64_t E, int64_t N, int64_t K, const void* bank, int meta_layout,
+                    uint16_t* out, void* stream);
+
+/*
+ * One quantised linear y[m,n] = sum_k x[m,k] * dq(W[n,k]) through the same
+ * kernels as the MLP's down projection (GEMV) or its MFMA GEMM.
+ *   fmt WQ_FMT_FP8W: w = [N, K] E4M3 codes, scale = [N] float32, global_scale ignored
+ *   fmt WQ_FMT_NVFP4: w = Block64 [N, K/64], scale = NULL, global_scale as above
+ *   y [M, N] float32.  Workspace: qlinear_workspace_bytes.
+ */
+size_t qlinear_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K, int flags);
+int qlinear_run(int fmt, int64_t M, int64_t N, int64_t K, const void* x, int x_dtype,
+                const uint8_t* w, const float* scale, float global_scale,
+                void* workspace, size_t workspace_bytes, float* y, int flags, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WQMLP_H */

@@ -12,8 +12,8 @@
 import numpy as np
 
 
-def e4m3_to_f64(codes):
-    """Decode E4M3fn bytes to float64 exactly.
+def e4m3_fields_to_f64(codes):
+    """Decode E4M3fn bytes to float64 exactly from the bit fields.
 
     value = (-1)^s * 2^(e-7) * (1 + m/8) for e > 0, (-1)^s * m * 2^-9 for e == 0,
     NaN for e == 15 and m == 7.  0x80 decodes to -0.0.
@@ -29,8 +29,8 @@ def e4m3_to_f64(codes):
     return np.where((e == 15) & (m == 7), np.nan, val)
 
 
-def e2m1_to_f64(nibbles):
-    """Decode E2M1 nibbles (0..15) to float64 exactly.
+def e2m1_fields_to_f64(nibbles):
+    """Decode E2M1 nibbles (0..15) to float64 exactly from the bit fields.
 
     value = (-1)^s * 2^(e-1) * (1 + m/2) for e > 0, (-1)^s * m * 0.5 for e == 0.
     Magnitudes are {0, 0.5, 1, 1.5, 2, 3, 4, 6}; code 8 decodes to -0.0.
@@ -42,6 +42,22 @@ def e2m1_to_f64(nibbles):
     normal = np.ldexp(1.0 + m / 2.0, (e - 1).astype(np.int32))
     mag = np.where(e == 0, m * 0.5, normal)
     return np.where(s == 1, -mag, mag)
+
+
+# Large tensors are decoded through the 256 / 16 values the field decoders give for
+# every code (same definition, evaluated once per code instead of once per element).
+_E4M3_ALL = e4m3_fields_to_f64(np.arange(256))
+_E2M1_ALL = e2m1_fields_to_f64(np.arange(16))
+
+
+def e4m3_to_f64(codes):
+    """E4M3fn codes (uint8 array) -> float64, by the bit-field definition above."""
+    return _E4M3_ALL[np.asarray(codes, dtype=np.uint8)]
+
+
+def e2m1_to_f64(nibbles):
+    """E2M1 codes (0..15) -> float64, by the bit-field definition above."""
+    return _E2M1_ALL[np.asarray(nibbles).astype(np.uint8) & 15]
 
 
 def bf16_bits_to_f64(bits):

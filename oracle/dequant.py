@@ -23,7 +23,7 @@ def fp8w_dequant(w, scale):
 def nvfp4_inv_global(global_scale):
     """The runtime dequantisation factor 1/weight_global_scale, rounded once to float32
     (page "Qwen3.8-27B-NVFP4", section "NVFP4 numerics as implemented")."""
-    return np.float32(1.0 / np.float64(np.float32(global_scale)))
+    return np.float32(1.0) / np.float32(global_scale)      # IEEE float32 division: one rounding
 
 
 def nvfp4_dequant_parts(weight_packed, weight_scale, global_scale):

@@ -55,7 +55,7 @@ def nvfp4_weight_f64(blk, global_scale):
     nib[:, 0::2] = wp & 0x0F
     nib[:, 1::2] = wp >> 4
     d = np.repeat(e4m3_to_f64(ws), 16, axis=1)
-    inv = np.float64(np.float32(1.0 / np.float64(np.float32(global_scale))))
+    inv = np.float64(np.float32(1.0) / np.float32(global_scale))
     return e2m1_to_f64(nib) * d * inv
 
 

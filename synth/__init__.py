@@ -62,16 +62,18 @@ def to_f16_bits(v):
 
 
 def to_e2m1_codes(v):
-    """Nearest E2M1 code, ties to the even code, saturating at +-6; sign in bit 3."""
-    v = np.asarray(v, dtype=np.float32)
-    a = np.abs(v)
-    mids = np.array([(E2M1_VALUES[i] + E2M1_VALUES[i + 1]) / 2 for i in range(7)], dtype=np.float32)
-    hi = np.searchsorted(mids, a, side="right")            # code if rounding up at ties
-    lo = np.searchsorted(mids, a, side="left")             # code if rounding down at ties
-    tie = hi != lo
-    mag = np.where(tie, np.where(lo % 2 == 0, lo, hi), hi).astype(np.uint8)
-    sign = (np.signbit(v)).astype(np.uint8) << 3
-    return mag | sign
+    """Nearest E2M1 code, ties to the even code, saturating at +-6; sign in bit 3.
+
+    The value set {0, .5, 1, 1.5, 2, 3, 4, 6} has spacing 0.5 below 2, 1 in [2, 4)
+    and 2 from 4: round-half-even at that spacing and offset into the code range
+    (the even code is the even multiple at each tie).
+    """
+    t = torch.from_numpy(np.ascontiguousarray(v, dtype=np.float32))
+    a = t.abs()
+    c = torch.where(a < 2, torch.round(a * 2),
+                    torch.where(a < 4, torch.round(a) + 2, torch.clamp(torch.round(a * 0.5) + 4, max=7)))
+    sign = torch.signbit(t).to(torch.uint8) << 3
+    return (c.to(torch.uint8) | sign).numpy()
 
 
 # ---- workloads ---------------------------------------------------------------------------------
@@ -106,17 +108,18 @@ def fp8_mlp(M=1, H=5120, I=17408, config_id=2, std=0.02):
 
 def nvfp4_tensor(N, K, config_id, tensor_id, std=0.02):
     """Recipe 3 for one tensor -> (weight_packed [N,K/2] u8, weight_scale [N,K/16] u8, global_scale f32)."""
-    w = rng(config_id, tensor_id).standard_normal((N, K), dtype=np.float32) * np.float32(std)
-    amax = np.float32(np.max(np.abs(w)))
+    w = torch.from_numpy(rng(config_id, tensor_id).standard_normal((N, K), dtype=np.float32))
+    w.mul_(std)
+    amax = np.float32(w.abs().max().item())
     gs = np.float32(E4M3_MAX * 6.0) / amax
-    g = w.reshape(N, K // 16, 16)
-    gmax = np.max(np.abs(g), axis=2)
-    d_codes = to_e4m3_codes(gmax / np.float32(6.0) * gs)
+    g = w.view(N, K // 16, 16)
+    gmax = g.abs().amax(dim=2)
+    d_codes = to_e4m3_codes((gmax / 6.0 * float(gs)).numpy())
     d_codes = np.where(d_codes == 0, np.uint8(1), d_codes).astype(np.uint8)   # keep the group scale positive
-    d_val = e4m3_codes_as_f32(d_codes)
-    q = to_e2m1_codes(g * (gs / d_val)[:, :, None]).reshape(N, K)
+    d_val = torch.from_numpy(e4m3_codes_as_f32(d_codes))
+    q = torch.from_numpy(to_e2m1_codes((g * (float(gs) / d_val)[:, :, None]).numpy())).view(N, K)
     del g, w
-    packed = (q[:, 0::2] | (q[:, 1::2] << 4)).astype(np.uint8)
+    packed = (q[:, 0::2] | (q[:, 1::2] << 4)).contiguous().numpy()
     return packed, d_codes, gs
 
 
@@ -143,15 +146,15 @@ def awq_quant(w):
     w float32 [..., N, K] -> (codes u8 [..., N, K], scales f16 bits [..., N, K/32], zeros u8 [..., N, K/32]).
     """
     shp = w.shape
-    g = w.reshape(*shp[:-1], shp[-1] // 32, 32)
-    mn = g.min(axis=-1)
-    mx = g.max(axis=-1)
-    s16 = ((mx - mn) / np.float32(15.0)).astype(np.float16)
-    s16 = np.where(s16 > 0, s16, np.float16(1e-3)).astype(np.float16)
-    s = s16.astype(np.float32)
-    z = np.clip(np.rint(-mn / s), 0, 15).astype(np.uint8)
-    q = np.clip(np.rint(g / s[..., None]) + z[..., None].astype(np.float32), 0, 15).astype(np.uint8)
-    return q.reshape(shp), s16.view(np.uint16), z
+    g = torch.from_numpy(np.ascontiguousarray(w, dtype=np.float32)).view(*shp[:-1], shp[-1] // 32, 32)
+    mn = g.amin(dim=-1)
+    mx = g.amax(dim=-1)
+    s16 = ((mx - mn) / 15.0).to(torch.float16)
+    s16 = torch.where(s16 > 0, s16, torch.tensor(1e-3, dtype=torch.float16))
+    s = s16.float()
+    z = torch.clamp(torch.round(-mn / s), 0, 15)
+    q = torch.clamp(torch.round(g / s[..., None]) + z[..., None], 0, 15).to(torch.uint8)
+    return (q.view(shp).numpy(), s16.numpy().view(np.uint16), z.to(torch.uint8).numpy())
 
 
 def awq_moe(E=512, topk=10, H=2560, I=160, config_id=5, std=0.02, expert_chunk=64):

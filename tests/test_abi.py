@@ -1,0 +1,147 @@
+"""Host-only checks of the C ABI: symbols, sizes and the argument-validation phase.
+
+Every call here returns from the pure-arithmetic validation phase before any HIP
+call, so these run on a machine without a GPU.  Pointers are fake addresses.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+import weight_quantized_mlp_amd as wq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "wqmlp.h")
+
+EINVAL, EALIGN, EOVERLAP, EWORKSPACE = -1, -2, -3, -6
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(wq.lib_path):
+        pytest.fail("libwqmlp.so is not built (run __graft_entry__.build())")
+    return wq.lib()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(\w+)\(", text, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = header_functions()
+    assert set(names) == {
+        "wq_abi_version", "wq_strerror", "wq_last_hip_error", "mlp_workspace_bytes", "mlp_fp8w_run",
+        "mlp_nvfp4_run", "awq_bank_bytes", "moe_awq_m1_run", "nvfp4_pack_block64", "awq_pack_bank",
+        "fp8w_dequant_f32", "nvfp4_dequant_f32", "awq_dequant_f16", "qlinear_workspace_bytes", "qlinear_run"}
+    for n in names:
+        assert hasattr(L, n), n
+        assert n in wq.__all__ or n == "wq_last_hip_error", n
+
+
+def test_version_and_messages(L):
+    assert wq.wq_abi_version() == 1
+    for rc in range(0, -8, -1):
+        assert wq.wq_strerror(rc)
+    assert wq.wq_strerror(-99) == "unknown error"
+
+
+def test_workspace_queries(L):
+    assert wq.mlp_workspace_bytes(0, 1, 5120, 17408) == 17408 * 4
+    n = wq.mlp_workspace_bytes(1, 512, 5120, 17408)
+    assert n >= 512 * 5120 * 2 + 512 * 4 + 512 * 17408 * 2
+    assert wq.mlp_workspace_bytes(1, 4, 5120, 17408, "gemv") == 4 * 17408 * 4
+    assert wq.mlp_workspace_bytes(1, 4, 5120, 17408, "mfma") == 4 * 5120 * 2 + 256 + 4 * 17408 * 2
+    assert wq.mlp_workspace_bytes(7, 1, 64, 64) == 0
+    assert wq.mlp_workspace_bytes(0, 0, 64, 64) == 0
+    assert wq.qlinear_workspace_bytes(1, 4, 64, 64) == 0
+    assert wq.qlinear_workspace_bytes(1, 128, 64, 64) > 0
+
+
+@pytest.mark.parametrize("E,N,K", [(512, 320, 2560), (512, 2560, 160), (3, 64, 96)])
+@pytest.mark.parametrize("ml", [3, 4])
+def test_awq_bank_bytes_match_oracle_layout(L, E, N, K, ml):
+    assert wq.awq_bank_bytes(E, N, K, ml) == E * oracle.awq_bank_layout(N, K, ml)["expert_bytes"]
+    assert wq.awq_bank_bytes(E, N, K + 1, ml) == 0
+    assert wq.awq_bank_bytes(E, N, K, 5) == 0
+
+
+A = 1 << 32   # fake, 16-byte aligned device-looking addresses (never dereferenced)
+
+
+def fp8_args(**kw):
+    a = dict(M=1, H=64, I=128, x=A, dt=1, wg=A + 0x100000, sg=A + 0x200000, wu=A + 0x300000, su=A + 0x400000,
+             wd=A + 0x500000, sd=A + 0x600000, ws=A + 0x700000, wsb=1 << 20, out=A + 0x800000, flags=0, st=None)
+    a.update(kw)
+    return [a[k] for k in ("M", "H", "I", "x", "dt", "wg", "sg", "wu", "su", "wd", "sd", "ws", "wsb", "out", "flags",
+                           "st")]
+
+
+@pytest.mark.parametrize("kw,rc", [
+    (dict(x=None), EINVAL), (dict(wd=None), EINVAL), (dict(sg=None), EINVAL), (dict(out=None), EINVAL),
+    (dict(dt=2), EINVAL), (dict(dt=9), EINVAL), (dict(flags=3), EINVAL), (dict(M=-1), EINVAL),
+    (dict(H=0), EINVAL), (dict(H=72), EINVAL), (dict(I=40), EINVAL),
+    (dict(M=200, H=80), EINVAL),                        # MFMA path needs multiples of 64
+    (dict(x=A + 8), EALIGN), (dict(wg=A + 0x100004), EALIGN), (dict(sd=A + 0x600002), EALIGN),
+    (dict(out=A + 0x800008), EALIGN), (dict(ws=A + 0x700001), EALIGN),
+    (dict(ws=None), EWORKSPACE), (dict(wsb=128 * 4 - 1), EWORKSPACE),
+    (dict(out=A), EOVERLAP), (dict(out=A + 0x100000), EOVERLAP), (dict(ws=A + 0x600000), EOVERLAP),
+    (dict(ws=A + 0x800000), EOVERLAP),
+])
+def test_fp8_validation(L, kw, rc):
+    assert L.mlp_fp8w_run(*fp8_args(**kw)) == rc
+
+
+def test_empty_batch_is_ok(L):
+    assert L.mlp_fp8w_run(*fp8_args(M=0)) == 0
+
+
+def nv_args(**kw):
+    a = dict(M=1, H=64, I=128, x=A, dt=1, gb=A + 0x100000, gg=1.0, ub=A + 0x300000, ug=1.0,
+             db=A + 0x500000, dg=1.0, ws=A + 0x700000, wsb=1 << 20, out=A + 0x800000, flags=0, st=None)
+    a.update(kw)
+    return [a[k] for k in ("M", "H", "I", "x", "dt", "gb", "gg", "ub", "ug", "db", "dg", "ws", "wsb", "out",
+                           "flags", "st")]
+
+
+@pytest.mark.parametrize("kw,rc", [
+    (dict(H=96), EINVAL), (dict(I=32), EINVAL), (dict(gg=0.0), EINVAL), (dict(dg=-1.0), EINVAL),
+    (dict(ug=float("inf")), EINVAL), (dict(ug=float("nan")), EINVAL), (dict(db=None), EINVAL),
+    (dict(gb=A + 0x100004), EALIGN), (dict(ws=None), EWORKSPACE),
+    (dict(out=A + 0x500000), EOVERLAP),
+])
+def test_nvfp4_validation(L, kw, rc):
+    assert L.mlp_nvfp4_run(*nv_args(**kw)) == rc
+
+
+def moe_args(**kw):
+    a = dict(E=512, topk=10, H=2560, I=160, x=A, ids=A + 0x1000, rw=A + 0x2000, w13=A + 0x10000000,
+             w2=A + 0x40000000, ml=3, act=A + 0x3000, out=A + 0x4000, st=None)
+    a.update(kw)
+    return [a[k] for k in ("E", "topk", "H", "I", "x", "ids", "rw", "w13", "w2", "ml", "act", "out", "st")]
+
+
+@pytest.mark.parametrize("kw,rc", [
+    (dict(E=0), EINVAL), (dict(topk=0), EINVAL), (dict(topk=17), EINVAL), (dict(H=2561), EINVAL),
+    (dict(I=100), EINVAL), (dict(ml=5), EINVAL), (dict(ids=None), EINVAL), (dict(out=None), EINVAL),
+    (dict(x=A + 2), EALIGN), (dict(rw=A + 0x2004), EALIGN), (dict(w2=A + 0x40000008), EALIGN),
+    (dict(act=A + 0x10), EOVERLAP), (dict(out=A + 0x3000 + 64), EOVERLAP), (dict(out=A + 0x10000000 + 4096), EOVERLAP),
+])
+def test_moe_validation(L, kw, rc):
+    assert L.moe_awq_m1_run(*moe_args(**kw)) == rc
+
+
+def test_packer_and_decoder_validation(L):
+    assert L.nvfp4_pack_block64(4, 96, A, A + 4096, A + 8192, None) == EINVAL
+    assert L.nvfp4_pack_block64(4, 128, A, A + 4096, A + 128, None) == EOVERLAP
+    assert L.awq_pack_bank(2, 8, 33, A, A + 4096, A + 8192, 3, A + 16384, None) == EINVAL
+    assert L.awq_pack_bank(2, 8, 64, A, A + 4096, A + 8192, 3, A + 16388, None) == EALIGN
+    assert L.fp8w_dequant_f32(4, 16, A, None, A + 4096, None) == EINVAL
+    assert L.nvfp4_dequant_f32(4, 64, A, 0.0, A + 4096, None) == EINVAL
+    assert L.awq_dequant_f16(1, 8, 64, A, 4, A + 16, None) == EOVERLAP
+    assert L.qlinear_run(2, 1, 64, 64, A, 1, A + 4096, A + 8192, 1.0, None, 0, A + 12288, 0, None) == EINVAL
+    assert L.qlinear_run(0, 1, 64, 64, A, 1, A + 4096, None, 1.0, None, 0, A + 12288, 0, None) == EINVAL
+    assert L.qlinear_run(1, 128, 64, 64, A, 1, A + 4096, None, 1.0, None, 0, A + 1 << 20, 0, None) == EWORKSPACE

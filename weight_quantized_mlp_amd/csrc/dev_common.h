@@ -1,0 +1,115 @@
+// Device-side helpers shared by the gfx950 kernels of this library.
+//
+// Element decoders use the CDNA4 conversion instructions.  Their semantics were
+// established by exhaustive checks on gfx950:
+//   * v_cvt_pk_f32_fp8 decodes OCP E4M3 ("fn": bias 7, NaN at S.1111.111) exactly;
+//   * the v_cvt_scalef32_pk_* conversions take only the exponent of their float
+//     scale operand (a power of two), so they are used with scale 1.0, where they
+//     return the exact E2M1 / E4M3 value, and the E4M3 group / channel scale is
+//     applied by a separate exact or single-rounding multiply.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace wq {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x2 __attribute__((ext_vector_type(2)));
+
+// ---- element decoders ---------------------------------------------------------------------
+// Two E4M3 bytes (bytes 0,1 or 2,3 of w) -> two exact float32.
+template <bool HI>
+__device__ __forceinline__ f32x2 e4m3x2_f32(uint32_t w) {
+  return __builtin_amdgcn_cvt_pk_f32_fp8(w, HI);
+}
+// Two E4M3 bytes -> two exact bf16 / f16 (every E4M3 value is representable in both).
+template <bool HI>
+__device__ __forceinline__ bf16x2 e4m3x2_bf16(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI);
+}
+template <bool HI>
+__device__ __forceinline__ f16x2 e4m3x2_f16(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI);
+}
+// Two E2M1 nibbles of byte B of w (low nibble first) -> exact float32 / bf16 / f16.
+template <int B>
+__device__ __forceinline__ f32x2 e2m1x2_f32(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, B);
+}
+template <int B>
+__device__ __forceinline__ bf16x2 e2m1x2_bf16(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, B);
+}
+template <int B>
+__device__ __forceinline__ f16x2 e2m1x2_f16(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, B);
+}
+// Single E4M3 byte B of w -> float32 (exact).
+template <int B>
+__device__ __forceinline__ float e4m3_byte_f32(uint32_t w) {
+  f32x2 v = __builtin_amdgcn_cvt_pk_f32_fp8(w, B >= 2);
+  return (B & 1) ? v.y : v.x;
+}
+
+// ---- bit reinterpretation ---------------------------------------------------------------------
+// Always reinterpret a scalar VALUE: in this toolchain __builtin_bit_cast applied to an
+// ext-vector element expression (v.y) reads the vector's first element instead.
+__device__ __forceinline__ f16x2 as_f16x2(uint32_t v) { return __builtin_bit_cast(f16x2, v); }
+__device__ __forceinline__ uint32_t as_u32(f16x2 v) { return __builtin_bit_cast(uint32_t, v); }
+
+// ---- dot products ---------------------------------------------------------------------------
+// acc + a.x*b.x + a.y*b.y with float32 accumulation (bf16 and f16 operands).
+__device__ __forceinline__ float dot2_bf16(bf16x2 a, uint32_t b_bits, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(a, __builtin_bit_cast(bf16x2, b_bits), acc, false);
+}
+__device__ __forceinline__ float dot2_f16(f16x2 a, f16x2 b, float acc) {
+  return __builtin_amdgcn_fdot2(a, b, acc, false);
+}
+
+// ---- reductions -----------------------------------------------------------------------------
+// Butterfly sum over groups of W lanes (W = 16 or 64): xor offsets W/2, ..., 1.
+// The order is fixed, so the result is bitwise reproducible and equal in all lanes.
+template <int W>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int off = W / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+__device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + expf(-z)); }
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+}  // namespace wq
+
+namespace wq {
+
+// ---- AWQ int4 group-32 -------------------------------------------------------------------------
+// A dword of a code chunk holds 8 consecutive k (byte b: low nibble k=2b, high k=2b+1),
+// i.e. the nibble of local k sits at bits [4k, 4k+4).  awq_pair<I> returns the pair
+// (local k = I, local k = I + 4) dequantised as RN_f16(q * s + b) with one rounding,
+// where b = RN_f16(-zero * s) is precomputed per group:
+//   (nibble | 0x6400) is the half 1024 + q, minus 1024 is exactly q; then one packed fma.
+template <int I>
+__device__ __forceinline__ f16x2 awq_pair(uint32_t w, f16x2 s2, f16x2 b2) {
+  const uint32_t t = ((w >> (4 * I)) & 0x000F000Fu) | 0x64006400u;
+  const f16x2 q = __builtin_bit_cast(f16x2, t) - f16x2{(_Float16)1024.0f, (_Float16)1024.0f};
+  return __builtin_elementwise_fma(q, s2, b2);
+}
+
+// Per-group bias RN_f16(-zero * scale), a single half multiply.
+__device__ __forceinline__ _Float16 awq_bias(uint32_t zero, _Float16 s) {
+  const _Float16 nz = -(_Float16)(float)zero;
+  return nz * s;
+}
+
+__device__ __forceinline__ _Float16 f16_from_bits(uint16_t b) { return __builtin_bit_cast(_Float16, b); }
+
+}  // namespace wq

@@ -1,0 +1,72 @@
+// Host-side launchers of the gfx950 kernels (internal to the library).
+// Argument checking happens in abi.cpp before any of these is called; the
+// launchers only compute launch shapes and enqueue.  Each returns the
+// hipError_t of the launch (hipGetLastError after the enqueue).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace wq {
+
+enum XType { X_F32 = 0, X_BF16 = 1, X_F16 = 2 };
+
+// ---- M < 128: split-K GEMV family -------------------------------------------------------------
+// FP8: y[m,n] = s0[n] * sum_k x[m,k] e4m3(w0[n,k]); with w1/s1 (gate+up) y = silu(g)*u.
+hipError_t launch_fp8w_gemv(int M, int K, int N, const void* x, XType xt,
+                            const uint8_t* w0, const float* s0, const uint8_t* w1, const float* s1,
+                            float* y, hipStream_t st);
+// NVFP4 Block64: same with the per-tensor factors inv0 = 1/gs0, inv1 = 1/gs1.
+hipError_t launch_nvfp4_gemv(int M, int K, int N, const void* x, XType xt,
+                             const uint8_t* b0, float inv0, const uint8_t* b1, float inv1,
+                             float* y, hipStream_t st);
+
+// ---- M >= 128: MFMA GEMM family ---------------------------------------------------------------
+// x [M,K] (f32 or bf16) -> x16 [M,K] f16 scaled per row by 2^-e, rowscale[m] = 2^e.
+hipError_t launch_rowscale_f16(int M, int K, const void* x, XType xt, uint16_t* x16, float* rowscale,
+                               hipStream_t st);
+// fmt 0 FP8 (w = [N,K] codes, colscale[n]) / 1 NVFP4 (w = Block64, uniform inv).
+// gate+up: act16[m,n] = f16(silu(g) * u) with g = rowscale[m]*colscale(n)*acc.
+hipError_t launch_mfma_gateup(int fmt, int M, int K, int N, const uint16_t* x16, const float* rowscale,
+                              const uint8_t* w0, const float* cs0, float inv0,
+                              const uint8_t* w1, const float* cs1, float inv1,
+                              uint16_t* act16, hipStream_t st);
+// single matrix: y[m,n] = rowscale[m] (1 if null) * colscale(n) * sum_k a16[m,k] dq(w[n,k]).
+hipError_t launch_mfma_linear(int fmt, int M, int K, int N, const uint16_t* a16, const float* rowscale,
+                              const uint8_t* w, const float* cs, float inv, float* y, hipStream_t st);
+
+// ---- AWQ routed-expert single-token step ------------------------------------------------------
+hipError_t launch_moe_awq_m1(int E, int topk, int H, int I, const uint16_t* x, const int32_t* ids,
+                             const float* router_w, const uint8_t* w13, const uint8_t* w2, int meta_layout,
+                             uint16_t* act, uint16_t* out, hipStream_t st);
+
+// ---- packers and debug decoders -------------------------------------------------------------
+hipError_t launch_nvfp4_pack(int64_t N, int64_t K, const uint8_t* wp, const uint8_t* ws, uint8_t* blk,
+                             hipStream_t st);
+hipError_t launch_awq_pack(int64_t E, int64_t N, int64_t K, const uint8_t* codes, const uint16_t* scales,
+                           const uint8_t* zeros, int meta_layout, uint8_t* bank, hipStream_t st);
+hipError_t launch_fp8w_dequant(int64_t N, int64_t K, const uint8_t* w, const float* s, float* out,
+                               hipStream_t st);
+hipError_t launch_nvfp4_dequant(int64_t N, int64_t K, const uint8_t* blk, float inv, float* out,
+                                hipStream_t st);
+hipError_t launch_awq_dequant(int64_t E, int64_t N, int64_t K, const uint8_t* bank, int meta_layout,
+                              uint16_t* out, hipStream_t st);
+
+// ---- AWQ bank geometry (shared by the packer, the decoder and the step) ------------------------
+struct AwqLayout {
+  int64_t G;           // groups of 32 per row
+  int64_t scale_off;   // byte offset of the f16 scale plane inside an expert
+  int64_t meta2_off;   // byte offset of the zero (u8) or bias (f16) plane
+  int64_t expert_bytes;
+};
+inline AwqLayout awq_layout(int64_t N, int64_t K, int meta_layout) {
+  auto r16 = [](int64_t v) { return (v + 15) / 16 * 16; };
+  AwqLayout L;
+  L.G = K / 32;
+  L.scale_off = r16(N * K / 2);
+  L.meta2_off = L.scale_off + r16(2 * N * L.G);
+  L.expert_bytes = L.meta2_off + r16((meta_layout == 3 ? 1 : 2) * N * L.G);
+  return L;
+}
+
+}  // namespace wq
