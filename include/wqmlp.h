@@ -53,8 +53,14 @@ enum {
   WQ_EWORKSPACE = -6, /* workspace missing or smaller than the query returns */
   WQ_ELAUNCH = -7     /* kernel launch failed; see wq_last_hip_error() */
 };
-/* path selection (flags): AUTO picks the MFMA GEMM for M >= WQ_MFMA_MIN_ROWS */
+/* path selection (flags bits 0-1): AUTO picks the MFMA GEMM for M >= WQ_MFMA_MIN_ROWS */
 enum { WQ_PATH_AUTO = 0, WQ_PATH_GEMV = 1, WQ_PATH_MFMA = 2 };
+/* stage selection (flags bits 2-3, MLP entry points only; default: both stages).
+ * GATEUP_ONLY enqueues the gate/up projection + SwiGLU, leaving act in the
+ * workspace; DOWN_ONLY enqueues the down projection from the act a previous
+ * GATEUP_ONLY call (same shape, path and workspace) left there.  For callers
+ * that interleave work or timing between the two stages. */
+enum { WQ_STAGE_GATEUP_ONLY = 4, WQ_STAGE_DOWN_ONLY = 8 };
 #define WQ_MFMA_MIN_ROWS 128
 /* largest top-k the routed-expert step accepts */
 #define WQ_MOE_MAX_TOPK 16
@@ -86,6 +92,7 @@ size_t mlp_workspace_bytes(int fmt, int64_t M, int64_t H, int64_t I, int flags);
  *   s_gate  [I]     float32 per-output-channel scales;  likewise w_up / s_up
  *   w_down  [H, I]  uint8 E4M3fn codes;  s_down [H] float32
  *   out     [M, H]  float32
+ * flags: WQ_PATH_* | optional WQ_STAGE_* bit.
  * Shapes: H, I > 0 and multiples of 16 (GEMV) or 64 (MFMA).  Accumulation is
  * float32; silu(z) = z / (1 + exp(-z)).  The GEMV path (M < 128 under AUTO)
  * reduces each output over k in a fixed order that does not depend on M, so

@@ -15,7 +15,7 @@ import torch
 
 __all__ = [
     "WQError", "lib", "lib_path", "WQ_F32", "WQ_BF16", "WQ_F16", "WQ_FMT_FP8W", "WQ_FMT_NVFP4",
-    "WQ_PATH_AUTO", "WQ_PATH_GEMV", "WQ_PATH_MFMA", "wq_abi_version", "wq_strerror",
+    "WQ_PATH_AUTO", "WQ_PATH_GEMV", "WQ_PATH_MFMA", "WQ_STAGE_GATEUP_ONLY", "WQ_STAGE_DOWN_ONLY", "wq_abi_version", "wq_strerror",
     "mlp_workspace_bytes", "mlp_fp8w_run", "mlp_nvfp4_run", "awq_bank_bytes", "moe_awq_m1_run",
     "nvfp4_pack_block64", "awq_pack_bank", "fp8w_dequant_f32", "nvfp4_dequant_f32", "awq_dequant_f16",
     "qlinear_workspace_bytes", "qlinear_run",
@@ -24,7 +24,9 @@ __all__ = [
 WQ_F32, WQ_BF16, WQ_F16 = 0, 1, 2
 WQ_FMT_FP8W, WQ_FMT_NVFP4 = 0, 1
 WQ_PATH_AUTO, WQ_PATH_GEMV, WQ_PATH_MFMA = 0, 1, 2
+WQ_STAGE_GATEUP_ONLY, WQ_STAGE_DOWN_ONLY = 4, 8
 _PATHS = {"auto": WQ_PATH_AUTO, "gemv": WQ_PATH_GEMV, "mfma": WQ_PATH_MFMA}
+_STAGES = {None: 0, "gateup": WQ_STAGE_GATEUP_ONLY, "down": WQ_STAGE_DOWN_ONLY}
 
 lib_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libwqmlp.so")
 _lib = None
@@ -132,7 +134,8 @@ def _workspace(nbytes, dev, workspace):
     return workspace
 
 
-def mlp_fp8w_run(x, w_gate, s_gate, w_up, s_up, w_down, s_down, out=None, workspace=None, path="auto"):
+def mlp_fp8w_run(x, w_gate, s_gate, w_up, s_up, w_down, s_down, out=None, workspace=None, path="auto",
+                 stage=None):
     """FP8 E4M3 per-channel SwiGLU MLP.  x [M,H] f32/bf16; w_gate/w_up [I,H] u8; w_down [H,I] u8; s_* f32."""
     dev = x.device
     M, H = x.shape
@@ -148,13 +151,14 @@ def mlp_fp8w_run(x, w_gate, s_gate, w_up, s_up, w_down, s_down, out=None, worksp
     nb = mlp_workspace_bytes(WQ_FMT_FP8W, M, H, I, path)
     ws = _workspace(nb, dev, workspace)
     rc = lib().mlp_fp8w_run(M, H, I, _ptr(x), _xdtype(x), _ptr(w_gate), _ptr(s_gate), _ptr(w_up), _ptr(s_up),
-                            _ptr(w_down), _ptr(s_down), _ptr(ws), ws.numel(), _ptr(out), _PATHS[path],
-                            _stream(dev))
+                            _ptr(w_down), _ptr(s_down), _ptr(ws), ws.numel(), _ptr(out),
+                            _PATHS[path] | _STAGES[stage], _stream(dev))
     _check("mlp_fp8w_run", rc)
     return out
 
 
-def mlp_nvfp4_run(x, gate_blk, gate_gs, up_blk, up_gs, down_blk, down_gs, out=None, workspace=None, path="auto"):
+def mlp_nvfp4_run(x, gate_blk, gate_gs, up_blk, up_gs, down_blk, down_gs, out=None, workspace=None, path="auto",
+                  stage=None):
     """NVFP4 Block64 SwiGLU MLP.  x [M,H]; gate/up_blk [I,H/64,36] u8; down_blk [H,I/64,36] u8; gs floats."""
     dev = x.device
     M, H = x.shape
@@ -170,7 +174,7 @@ def mlp_nvfp4_run(x, gate_blk, gate_gs, up_blk, up_gs, down_blk, down_gs, out=No
     ws = _workspace(nb, dev, workspace)
     rc = lib().mlp_nvfp4_run(M, H, I, _ptr(x), _xdtype(x), _ptr(gate_blk), float(gate_gs), _ptr(up_blk),
                              float(up_gs), _ptr(down_blk), float(down_gs), _ptr(ws), ws.numel(), _ptr(out),
-                             _PATHS[path], _stream(dev))
+                             _PATHS[path] | _STAGES[stage], _stream(dev))
     _check("mlp_nvfp4_run", rc)
     return out
 

@@ -108,6 +108,7 @@ bool gemv_fits(int fmt, int64_t K, int dt) {
 }
 
 int pick_path(int64_t M, int flags) {
+  flags &= 3;
   if (flags == WQ_PATH_GEMV || flags == WQ_PATH_MFMA) return flags;
   return M >= WQ_MFMA_MIN_ROWS ? WQ_PATH_MFMA : WQ_PATH_GEMV;
 }
@@ -140,7 +141,9 @@ bool shape_ok(int fmt, int path, int64_t H, int64_t I, int x_dtype) {
 int mlp_run(int fmt, int64_t M, int64_t H, int64_t I, const void* x, int x_dtype, const uint8_t* wg,
             const float* sg, float gg, const uint8_t* wu, const float* su, float gu, const uint8_t* wd,
             const float* sd, float gd, void* ws, size_t ws_bytes, float* out, int flags, void* stream) {
-  if (flags < WQ_PATH_AUTO || flags > WQ_PATH_MFMA) return WQ_EINVAL;
+  const int stage = flags & (WQ_STAGE_GATEUP_ONLY | WQ_STAGE_DOWN_ONLY);
+  if ((flags & ~15) || (flags & 3) == 3 || stage == (WQ_STAGE_GATEUP_ONLY | WQ_STAGE_DOWN_ONLY)) return WQ_EINVAL;
+  const bool do_gu = stage != WQ_STAGE_DOWN_ONLY, do_down = stage != WQ_STAGE_GATEUP_ONLY;
   if (x_dtype != WQ_F32 && x_dtype != WQ_BF16) return WQ_EINVAL;
   if (M < 0 || M > kMaxDim) return WQ_EINVAL;
   const int path = pick_path(M, flags);
@@ -154,7 +157,7 @@ int mlp_run(int fmt, int64_t M, int64_t H, int64_t I, const void* x, int x_dtype
   if (M == 0) return WQ_OK;
   if (!all_aligned({x, wg, wu, wd, out, ws})) return WQ_EALIGN;
   if (fmt == WQ_FMT_FP8W && !all_aligned({sg, su, sd})) return WQ_EALIGN;
-  const size_t need = mlp_ws(fmt, M, H, I, flags);
+  const size_t need = mlp_ws(fmt, M, H, I, flags & 3);
   if (ws == nullptr || ws_bytes < need) return WQ_EWORKSPACE;
   const size_t nx = (size_t)M * H * xsize(x_dtype);
   const size_t nw_gu = wbytes(fmt, I, H), nw_d = wbytes(fmt, H, I);
@@ -171,11 +174,12 @@ int mlp_run(int fmt, int64_t M, int64_t H, int64_t I, const void* x, int x_dtype
   if (path == WQ_PATH_GEMV) {
     float* act = reinterpret_cast<float*>(ws);
     if (fmt == WQ_FMT_FP8W) {
-      rc = launched(wq::launch_fp8w_gemv(m, h, i, x, xt, wg, sg, wu, su, act, st));
-      if (rc == WQ_OK) rc = launched(wq::launch_fp8w_gemv(m, i, h, act, wq::X_F32, wd, sd, nullptr, nullptr, out, st));
+      if (do_gu) rc = launched(wq::launch_fp8w_gemv(m, h, i, x, xt, wg, sg, wu, su, act, st));
+      if (rc == WQ_OK && do_down)
+        rc = launched(wq::launch_fp8w_gemv(m, i, h, act, wq::X_F32, wd, sd, nullptr, nullptr, out, st));
     } else {
-      rc = launched(wq::launch_nvfp4_gemv(m, h, i, x, xt, wg, 1.0f / gg, wu, 1.0f / gu, act, st));
-      if (rc == WQ_OK)
+      if (do_gu) rc = launched(wq::launch_nvfp4_gemv(m, h, i, x, xt, wg, 1.0f / gg, wu, 1.0f / gu, act, st));
+      if (rc == WQ_OK && do_down)
         rc = launched(wq::launch_nvfp4_gemv(m, i, h, act, wq::X_F32, wd, 1.0f / gd, nullptr, 0.f, out, st));
     }
     return rc;
@@ -185,11 +189,14 @@ int mlp_run(int fmt, int64_t M, int64_t H, int64_t I, const void* x, int x_dtype
   float* rs = reinterpret_cast<float*>(base + align256((size_t)M * H * 2));
   uint16_t* act16 = reinterpret_cast<uint16_t*>(base + align256((size_t)M * H * 2) + align256((size_t)M * 4));
   const int f = fmt == WQ_FMT_NVFP4 ? 1 : 0;
-  rc = launched(wq::launch_rowscale_f16(m, h, x, xt, x16, rs, st));
-  if (rc == WQ_OK)
-    rc = launched(wq::launch_mfma_gateup(f, m, h, i, x16, rs, wg, sg, f ? 1.0f / gg : 0.f, wu, su,
-                                         f ? 1.0f / gu : 0.f, act16, st));
-  if (rc == WQ_OK) rc = launched(wq::launch_mfma_linear(f, m, i, h, act16, nullptr, wd, sd, f ? 1.0f / gd : 0.f, out, st));
+  if (do_gu) {
+    rc = launched(wq::launch_rowscale_f16(m, h, x, xt, x16, rs, st));
+    if (rc == WQ_OK)
+      rc = launched(wq::launch_mfma_gateup(f, m, h, i, x16, rs, wg, sg, f ? 1.0f / gg : 0.f, wu, su,
+                                           f ? 1.0f / gu : 0.f, act16, st));
+  }
+  if (rc == WQ_OK && do_down)
+    rc = launched(wq::launch_mfma_linear(f, m, i, h, act16, nullptr, wd, sd, f ? 1.0f / gd : 0.f, out, st));
   return rc;
 }
 
@@ -216,8 +223,8 @@ const char* wq_strerror(int rc) {
 int wq_last_hip_error(void) { return g_last_hip; }
 
 size_t mlp_workspace_bytes(int fmt, int64_t M, int64_t H, int64_t I, int flags) {
-  if ((fmt != WQ_FMT_FP8W && fmt != WQ_FMT_NVFP4) || flags < WQ_PATH_AUTO || flags > WQ_PATH_MFMA) return 0;
-  return mlp_ws(fmt, M, H, I, flags);
+  if ((fmt != WQ_FMT_FP8W && fmt != WQ_FMT_NVFP4) || (flags & ~15) || (flags & 3) == 3) return 0;
+  return mlp_ws(fmt, M, H, I, flags & 3);
 }
 
 int mlp_fp8w_run(int64_t M, int64_t H, int64_t I, const void* x, int x_dtype, const uint8_t* w_gate,
