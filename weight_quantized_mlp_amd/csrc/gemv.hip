@@ -1,6 +1,7 @@
-// M < 128 path: bandwidth-bound split-K GEMV kernels for FP8 E4M3 per-channel and
-// NVFP4 Block64 weights, with an optional fused SwiGLU epilogue (gate + up share
-// one activation load).
+// M < 128 path, general kernels: split-K GEMVs for FP8 E4M3 per-channel and NVFP4
+// Block64 weights, with an optional fused SwiGLU epilogue (gate + up share one
+// activation load).  They serve the shapes the main kernels in gemv_fast.hip do not
+// cover (float32 activations into gate+up, very long rows).
 //
 // Method: issue "tp>1 fp8w tail-MLP shard host-dequantizes every layer", section
 // "Proposed fix" (the MLP equation); FP8 decode from section "Mechanism on the tp>1
@@ -450,6 +451,7 @@ hipError_t nvfp4_dispatch(int M, int K, int N, const void* x, const uint8_t* b0,
 hipError_t launch_fp8w_gemv(int M, int K, int N, const void* x, XType xt, const uint8_t* w0, const float* s0,
                             const uint8_t* w1, const float* s1, float* y, hipStream_t st) {
   const bool gu = w1 != nullptr;
+  if (fast_gemv_fp8_ok(K, xt, gu)) return launch_fast_fp8(M, K, N, x, xt, w0, s0, w1, s1, y, st);
   if (xt == X_BF16)
     return gu ? fp8_dispatch<uint16_t, true>(M, K, N, x, w0, s0, w1, s1, y, st)
               : fp8_dispatch<uint16_t, false>(M, K, N, x, w0, s0, w1, s1, y, st);
@@ -460,6 +462,7 @@ hipError_t launch_fp8w_gemv(int M, int K, int N, const void* x, XType xt, const 
 hipError_t launch_nvfp4_gemv(int M, int K, int N, const void* x, XType xt, const uint8_t* b0, float inv0,
                              const uint8_t* b1, float inv1, float* y, hipStream_t st) {
   const bool gu = b1 != nullptr;
+  if (fast_gemv_nvfp4_ok(K, xt, gu)) return launch_fast_nvfp4(M, K, N, x, xt, b0, inv0, b1, inv1, y, st);
   if (xt == X_BF16)
     return gu ? nvfp4_dispatch<uint16_t, true>(M, K, N, x, b0, inv0, b1, inv1, y, st)
               : nvfp4_dispatch<uint16_t, false>(M, K, N, x, b0, inv0, b1, inv1, y, st);

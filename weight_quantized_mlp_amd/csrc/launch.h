@@ -21,6 +21,15 @@ hipError_t launch_nvfp4_gemv(int M, int K, int N, const void* x, XType xt,
                              const uint8_t* b0, float inv0, const uint8_t* b1, float inv1,
                              float* y, hipStream_t st);
 
+// Main M < 128 kernels (gemv_fast.hip); the *_ok predicates say whether a shape is covered.
+// For a given shape the same family serves every M < 128, so row results do not depend on M.
+bool fast_gemv_fp8_ok(int K, XType xt, bool gu);
+bool fast_gemv_nvfp4_ok(int K, XType xt, bool gu);
+hipError_t launch_fast_fp8(int M, int K, int N, const void* x, XType xt, const uint8_t* w0, const float* s0,
+                           const uint8_t* w1, const float* s1, float* y, hipStream_t st);
+hipError_t launch_fast_nvfp4(int M, int K, int N, const void* x, XType xt, const uint8_t* b0, float inv0,
+                             const uint8_t* b1, float inv1, float* y, hipStream_t st);
+
 // ---- M >= 128: MFMA GEMM family ---------------------------------------------------------------
 // x [M,K] (f32 or bf16) -> x16 [M,K] f16 scaled per row by 2^-e, rowscale[m] = 2^e.
 hipError_t launch_rowscale_f16(int M, int K, const void* x, XType xt, uint16_t* x16, float* rowscale,
