@@ -50,6 +50,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle baseline sample")
     ap.add_argument("--calib-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration for rocprofv3 --pmc)")
+    ap.add_argument("--counters", type=int, default=0,
+                    help="only run this many plain (non-graph) headline steps, for rocprofv3 --pmc passes")
     ap.add_argument("--json-out", default=None)
     return ap.parse_args()
 
@@ -267,6 +269,20 @@ def main():
         log("calibration copy done: 3 x 1 GiB device-to-device")
         return
 
+    if args.counters:
+        d = synth.fp8_mlp(M=1)
+        names = ("w_gate", "s_gate", "w_up", "s_up", "w_down", "s_down")
+        base = [torch.from_numpy(d[n]).to(dev) for n in names]
+        sets = [base] + [[t.clone() for t in base] for _ in range(3)]
+        x = torch.from_numpy(d["x_bits"].view("int16")).to(dev).view(torch.bfloat16)
+        out = torch.empty((1, H), dtype=torch.float32, device=dev)
+        ws = torch.empty(wq.mlp_workspace_bytes(wq.WQ_FMT_FP8W, 1, H, I), dtype=torch.uint8, device=dev)
+        for i in range(args.counters):
+            wq.mlp_fp8w_run(x, *sets[i % 4], out=out, workspace=ws)
+        torch.cuda.synchronize()
+        log(f"counter steps done: {args.counters}")
+        return
+
     K, W = args.steps, args.warmup
     log(f"fp8 decode: K={K} W={W}")
     r = fp8_decode(torch, wq, synth, K, W)
@@ -276,8 +292,8 @@ def main():
     dn_gbs = r["dn_alg"] / (r["dn_ms"] / 1e3) / 1e9
     log(f"fp8 decode: {t / K * 1e6:.2f} us/step, {gbs:.1f} GB/s; gate/up {r['gu_ms'] * 1e3:.2f} us "
         f"({gu_gbs:.0f} GB/s), down {r['dn_ms'] * 1e3:.2f} us ({dn_gbs:.0f} GB/s)")
-    traffic = read_traffic("fp8w_gemv_gateup_5120x17408_counters.txt",
-                           ["weight_quantized_mlp_amd/csrc/gemv.hip", "weight_quantized_mlp_amd/csrc/dev_common.h"])
+    traffic = read_traffic("fp8w_gateup_row_5120x17408_counters.txt",
+                           ["weight_quantized_mlp_amd/csrc/gemv_fast.hip", "weight_quantized_mlp_amd/csrc/dev_common.h"])
 
     extras = {}
     want = set() if args.extras == "none" else (
@@ -321,7 +337,7 @@ def main():
     cpu = cpu_baseline(oracle, r["data"], args.cpu_seconds)
     log("cpu", cpu)
 
-    roof = dict(bound="hbm", kernel="fp8w_gemv gate+up (SwiGLU) 5120x17408", achieved=round(gu_gbs, 1),
+    roof = dict(bound="hbm", kernel="fp8_gu_row (gate+up+SwiGLU) 5120x17408 M=1", achieved=round(gu_gbs, 1),
                 peak=HBM_PEAK_GBS, unit="GB/s", frac=round(gu_gbs / HBM_PEAK_GBS, 4),
                 traffic=traffic, algorithmic_bytes_per_launch=r["gu_alg"],
                 avg_launch_us=round(r["gu_ms"] * 1e3, 3),

@@ -202,9 +202,25 @@ __device__ __forceinline__ void stage_units(uint8_t* lds, const XT* __restrict__
   }
 }
 
+// Item cursor: item it = g * T + t advanced by NW per step without divisions.
+struct ItemCursor {
+  int g, t;
+  __device__ __forceinline__ void init(int it, int T) {
+    g = it / T;
+    t = it - g * T;
+  }
+  __device__ __forceinline__ void step(int nw, int T) {
+    t += nw;
+    while (t >= T) {
+      t -= T;
+      ++g;
+    }
+  }
+};
+
 // FP8 single linear: y[m, n] = s[n] * sum_k xa[m, k] e4m3(w[n, k]); XT float or bf16 bits.
-template <typename XT>
-__global__ void __launch_bounds__(64 * kItemWaves) fp8_lin_items(int M, int K, int N, const XT* __restrict__ xa,
+template <typename XT, bool ONE>
+__global__ void __launch_bounds__(64 * kItemWaves, 8) fp8_lin_items(int M, int K, int N, const XT* __restrict__ xa,
                                                                  const uint8_t* __restrict__ w,
                                                                  const float* __restrict__ s, float* __restrict__ y) {
   constexpr int R = 2, D = kItemDepth, NW = kItemWaves, RB = kItemRows;
@@ -216,23 +232,30 @@ __global__ void __launch_bounds__(64 * kItemWaves) fp8_lin_items(int M, int K, i
   const int rbase = blockIdx.x * RB;
   const int NI = (RB / R) * T;
   const int nk = NI > wv ? (NI - wv + NW - 1) / NW : 0;
-  for (int m = 0; m < M; ++m) {
+  const int Mloop = ONE ? 1 : M;
+  for (int m = 0; m < Mloop; ++m) {
     if (m) __syncthreads();
     for (int i = threadIdx.x; i < NW * RB; i += blockDim.x) (&part[0][0])[i] = 0.f;
     u32x4 buf[D][R];
-    auto load = [&](int k, int b) {
-      if (k >= nk) return;
-      const int it = wv + NW * k, g = it / T, t = it - g * T, c = lane + 64 * t;
-      if (c < C) {
+    ItemCursor lc;  // next item to load
+    lc.init(wv, T);
+    int lk = 0;
+    auto load = [&](int b) {
+      if (lk < nk) {
+        const int c = lane + 64 * lc.t;
+        if (c < C) {
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-          const int n = rbase + g * R + r;
-          if (n < N) buf[b][r] = ld_stream(w + (size_t)n * K + 16 * c);
+          for (int r = 0; r < R; ++r) {
+            const int n = rbase + lc.g * R + r;
+            if (n < N) buf[b][r] = ld_stream(w + (size_t)n * K + 16 * c);
+          }
         }
       }
+      ++lk;
+      lc.step(NW, T);
     };
 #pragma unroll
-    for (int b = 0; b < D; ++b) load(b, b);
+    for (int b = 0; b < D; ++b) load(b);
     stage_units<XT, 16>(lds, xa + (size_t)m * K, C);
     __syncthreads();
     float acc[R][2];
@@ -248,12 +271,15 @@ __global__ void __launch_bounds__(64 * kItemWaves) fp8_lin_items(int M, int K, i
         if (lane == 0) part[wv][cur * R + r] = v;
       }
     };
+    ItemCursor cc;  // item being computed
+    cc.init(wv, T);
     for (int k0 = 0; k0 < nk; k0 += D) {
 #pragma unroll
       for (int b = 0; b < D; ++b) {
         const int k = k0 + b;
         if (k < nk) {
-          const int it = wv + NW * k, g = it / T, t = it - g * T, c = lane + 64 * t;
+          const int g = cc.g, c = lane + 64 * cc.t;
+          cc.step(NW, T);
           if (g != cur) {
             flush();
             cur = g;
@@ -295,7 +321,7 @@ __global__ void __launch_bounds__(64 * kItemWaves) fp8_lin_items(int M, int K, i
               }
             }
           }
-          load(k + D, b);
+          load(b);
         }
       }
     }
@@ -314,8 +340,8 @@ __global__ void __launch_bounds__(64 * kItemWaves) fp8_lin_items(int M, int K, i
 }
 
 // NVFP4 single linear: y[m, n] = inv * sum_k xa[m, k] dq(blk[n, k]).
-template <typename XT>
-__global__ void __launch_bounds__(64 * kItemWaves) nv_lin_items(int M, int K, int N, const XT* __restrict__ xa,
+template <typename XT, bool ONE>
+__global__ void __launch_bounds__(64 * kItemWaves, 8) nv_lin_items(int M, int K, int N, const XT* __restrict__ xa,
                                                                 const uint8_t* __restrict__ blk, float inv,
                                                                 float* __restrict__ y) {
   constexpr int D = kItemDepth, NW = kItemWaves, RB = kItemRows;
@@ -327,24 +353,30 @@ __global__ void __launch_bounds__(64 * kItemWaves) nv_lin_items(int M, int K, in
   const int rbase = blockIdx.x * RB;
   const int NI = RB * T;
   const int nk = NI > wv ? (NI - wv + NW - 1) / NW : 0;
-  for (int m = 0; m < M; ++m) {
+  const int Mloop = ONE ? 1 : M;
+  for (int m = 0; m < Mloop; ++m) {
     if (m) __syncthreads();
     for (int i = threadIdx.x; i < NW * RB; i += blockDim.x) (&part[0][0])[i] = 0.f;
     u32x4 A[D], B[D];
     uint32_t Cw[D];
-    auto load = [&](int k, int b) {
-      if (k >= nk) return;
-      const int it = wv + NW * k, g = it / T, t = it - g * T, r = lane + 64 * t;
-      const int n = rbase + g;
-      if (r < nrec && n < N) {
-        const uint8_t* p = blk + (size_t)n * rb + (size_t)r * 36;
-        A[b] = ld16a4(p);
-        B[b] = ld16a4(p + 16);
-        Cw[b] = *reinterpret_cast<const uint32_t*>(p + 32);
+    ItemCursor lc;
+    lc.init(wv, T);
+    int lk = 0;
+    auto load = [&](int b) {
+      if (lk < nk) {
+        const int r = lane + 64 * lc.t, n = rbase + lc.g;
+        if (r < nrec && n < N) {
+          const uint8_t* p = blk + (size_t)n * rb + (size_t)r * 36;
+          A[b] = ld16a4(p);
+          B[b] = ld16a4(p + 16);
+          Cw[b] = *reinterpret_cast<const uint32_t*>(p + 32);
+        }
       }
+      ++lk;
+      lc.step(NW, T);
     };
 #pragma unroll
-    for (int b = 0; b < D; ++b) load(b, b);
+    for (int b = 0; b < D; ++b) load(b);
     stage_units<XT, 64>(lds, xa + (size_t)m * K, nrec);
     __syncthreads();
     float acc = 0.f;
@@ -355,12 +387,15 @@ __global__ void __launch_bounds__(64 * kItemWaves) nv_lin_items(int M, int K, in
       acc = 0.f;
       if (lane == 0) part[wv][cur] = v;
     };
+    ItemCursor cc;
+    cc.init(wv, T);
     for (int k0 = 0; k0 < nk; k0 += D) {
 #pragma unroll
       for (int b = 0; b < D; ++b) {
         const int k = k0 + b;
         if (k < nk) {
-          const int it = wv + NW * k, g = it / T, t = it - g * T, r = lane + 64 * t;
+          const int g = cc.g, r = lane + 64 * cc.t;
+          cc.step(NW, T);
           if (g != cur) {
             flush();
             cur = g;
@@ -405,7 +440,7 @@ __global__ void __launch_bounds__(64 * kItemWaves) nv_lin_items(int M, int K, in
               acc = fmaf(pt, e4m3_group(d, gq), acc);
             }
           }
-          load(k + D, b);
+          load(b);
         }
       }
     }
@@ -466,15 +501,19 @@ hipError_t launch_fast_fp8(int M, int K, int N, const void* x, XType xt, const u
   }
   const size_t lds = (size_t)K * (xt == X_F32 ? 4 : 2);
   const dim3 grid((N + kItemRows - 1) / kItemRows), block(64 * kItemWaves);
+#define WQ_LAUNCH(T, O)                                                                                     \
+  do {                                                                                                      \
+    if (!lds_ok(fp8_lin_items<T, O>, lds)) return hipErrorInvalidValue;                                     \
+    hipLaunchKernelGGL((fp8_lin_items<T, O>), grid, block, lds, st, M, K, N, reinterpret_cast<const T*>(x), w0, s0, y); \
+  } while (0)
   if (xt == X_F32) {
-    if (!lds_ok(fp8_lin_items<float>, lds)) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(fp8_lin_items<float>, grid, block, lds, st, M, K, N, reinterpret_cast<const float*>(x), w0, s0,
-                       y);
+    if (M == 1) WQ_LAUNCH(float, true);
+    else WQ_LAUNCH(float, false);
   } else {
-    if (!lds_ok(fp8_lin_items<uint16_t>, lds)) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(fp8_lin_items<uint16_t>, grid, block, lds, st, M, K, N, reinterpret_cast<const uint16_t*>(x),
-                       w0, s0, y);
+    if (M == 1) WQ_LAUNCH(uint16_t, true);
+    else WQ_LAUNCH(uint16_t, false);
   }
+#undef WQ_LAUNCH
   return hipGetLastError();
 }
 
@@ -499,15 +538,19 @@ hipError_t launch_fast_nvfp4(int M, int K, int N, const void* x, XType xt, const
   }
   const size_t lds = (size_t)K * (xt == X_F32 ? 4 : 2);
   const dim3 grid((N + kItemRows - 1) / kItemRows), block(64 * kItemWaves);
+#define WQ_LAUNCH(T, O)                                                                                      \
+  do {                                                                                                       \
+    if (!lds_ok(nv_lin_items<T, O>, lds)) return hipErrorInvalidValue;                                       \
+    hipLaunchKernelGGL((nv_lin_items<T, O>), grid, block, lds, st, M, K, N, reinterpret_cast<const T*>(x), b0, inv0, y); \
+  } while (0)
   if (xt == X_F32) {
-    if (!lds_ok(nv_lin_items<float>, lds)) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(nv_lin_items<float>, grid, block, lds, st, M, K, N, reinterpret_cast<const float*>(x), b0, inv0,
-                       y);
+    if (M == 1) WQ_LAUNCH(float, true);
+    else WQ_LAUNCH(float, false);
   } else {
-    if (!lds_ok(nv_lin_items<uint16_t>, lds)) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(nv_lin_items<uint16_t>, grid, block, lds, st, M, K, N, reinterpret_cast<const uint16_t*>(x),
-                       b0, inv0, y);
+    if (M == 1) WQ_LAUNCH(uint16_t, true);
+    else WQ_LAUNCH(uint16_t, false);
   }
+#undef WQ_LAUNCH
   return hipGetLastError();
 }
 
