@@ -242,13 +242,12 @@ __global__ void __launch_bounds__(64 * kItemWaves, 8) fp8_lin_items(int M, int K
     int lk = 0;
     auto load = [&](int b) {
       if (lk < nk) {
-        const int c = lane + 64 * lc.t;
-        if (c < C) {
+        // Clamped to the last chunk / row: in bounds, and never accumulated or stored.
+        const int c = min(lane + 64 * lc.t, C - 1);
 #pragma unroll
-          for (int r = 0; r < R; ++r) {
-            const int n = rbase + lc.g * R + r;
-            if (n < N) buf[b][r] = ld_stream(w + (size_t)n * K + 16 * c);
-          }
+        for (int r = 0; r < R; ++r) {
+          const int n = min(rbase + lc.g * R + r, N - 1);
+          buf[b][r] = ld_stream(w + (size_t)n * K + 16 * c);
         }
       }
       ++lk;
@@ -364,13 +363,12 @@ __global__ void __launch_bounds__(64 * kItemWaves, 8) nv_lin_items(int M, int K,
     int lk = 0;
     auto load = [&](int b) {
       if (lk < nk) {
-        const int r = lane + 64 * lc.t, n = rbase + lc.g;
-        if (r < nrec && n < N) {
-          const uint8_t* p = blk + (size_t)n * rb + (size_t)r * 36;
-          A[b] = ld16a4(p);
-          B[b] = ld16a4(p + 16);
-          Cw[b] = *reinterpret_cast<const uint32_t*>(p + 32);
-        }
+        // Clamped to the last record / row: in bounds, and never accumulated or stored.
+        const int r = min(lane + 64 * lc.t, nrec - 1), n = min(rbase + lc.g, N - 1);
+        const uint8_t* p = blk + (size_t)n * rb + (size_t)r * 36;
+        A[b] = ld16a4(p);
+        B[b] = ld16a4(p + 16);
+        Cw[b] = *reinterpret_cast<const uint32_t*>(p + 32);
       }
       ++lk;
       lc.step(NW, T);
