@@ -6,28 +6,31 @@
 // scale applied at every K=16 boundary).
 //
 // Two kernel shapes, chosen from measurements of the 5120 x 17408 decode:
-//  * row kernels (gate+up): one wave per output row pair; every weight load of the
-//    pair is issued at once (2 x 5 KB for FP8 at K=5120), the activation row sits in
-//    registers (FP8) or LDS (NVFP4), occupancy 8 waves/SIMD.  The weights stay in
+//  * row kernels (gate+up): one wave per output row pair (gate row n, up row n); every weight load of the
+//    pair is issued at once (2 x 5 KB for FP8 at K=5120), then the workgroup stages the activation row in
+//    LDS (one copy per 8 row pairs instead of one per wave); occupancy 8 waves/SIMD.  The weights stay in
 //    registers while the m rows of a multi-row call are processed one by one.
-//  * item kernels (down projection / single linear): a 16-wave workgroup owns RB
-//    output rows; the activation row is staged once into LDS; the (row pair, K slot)
-//    work items -- a K slot is one 16-byte load per lane -- are dealt round-robin to the
-//    waves, each wave streaming its items with the next D loads in flight; each wave
-//    keeps one partial per row it touches and the workgroup adds the 16 partials of a
+//  * item kernels (down projection / single linear): a 16-wave workgroup owns RB output rows; the
+//    activation row is staged once into LDS; the (row pair, K slot) work items -- a K slot is one unit per
+//    lane -- are dealt round-robin to the waves, each wave streaming its items with the next D loads in
+//    flight; each wave keeps one partial per row it touches and the workgroup adds the 16 partials of a
 //    row in wave order.
-// Fixed accumulation orders (bitwise reproducible; independent of M because m rows
-// are processed one after another with the same schedule):
-//  * FP8 row kernel: lane l owns 16-byte chunks l, l+64, ...; per chunk the 8 code pairs
-//    go into two partials (even / odd 4-code quads), chunks ascending; s = p0 + p1;
-//    butterfly over 64 lanes (xor 32..1); times the channel scale.
-//  * NVFP4 row kernel: lane l owns records l, l+64, ...; per record each K=16 group's
-//    partial (ascending k) is multiplied by its E4M3 scale and added in group order;
-//    butterfly over 64 lanes; times 1/global_scale.
-//  * item kernels: within a wave, items ascending, each item a chunk (FP8: 16 codes, two
-//    partials as above; NVFP4: one record as above); per row a butterfly over 64 lanes
-//    when the wave leaves the row; then the workgroup sums the per-wave partials in wave
-//    order 0..15; times the channel scale or 1/global_scale.
+// The per-lane unit is 16 weights for both formats: an FP8 chunk (16 code bytes) or an NVFP4 group (the
+// 8 nibble bytes qs[8q..8q+7] of a Block64 record and its scale byte d[q]).  Four lanes read one record,
+// so the 36-byte records are covered without gaps and K = 5120 fills every lane (320 groups per row).
+// Weight loads use clamped in-bounds addresses where a lane or item runs past the matrix and only the
+// accumulation is guarded: a guarded load makes the compiler drain all outstanding loads before the
+// next one.
+// Fixed accumulation orders (bitwise reproducible; independent of M because m rows are processed one
+// after another with the same schedule):
+//  * FP8 units: the 8 code pairs go into two partials (even / odd 4-code quads); NVFP4 units: one
+//    partial over the 16 weights in ascending k, then multiplied by the E4M3 group scale.
+//  * row kernels: lane l owns units l, l+64, ... (ascending); FP8 s = p0 + p1 per row, NVFP4 the scaled
+//    group partials summed in unit order; butterfly over 64 lanes (xor 32..1); times the channel scale
+//    or 1/global_scale.
+//  * item kernels: within a wave, items ascending, per row a butterfly over 64 lanes when the wave leaves
+//    the row; then the workgroup sums the per-wave partials in wave order 0..15; times the channel scale
+//    or 1/global_scale.
 #include "dev_common.h"
 #include "launch.h"
 
@@ -38,9 +41,16 @@ namespace {
 constexpr int kItemWaves = 16;   // waves per item-kernel workgroup
 constexpr int kItemRows = 20;    // output rows per item-kernel workgroup
 constexpr int kItemDepth = 2;    // loads in flight per wave (items)
+constexpr int kRowWaves = 8;     // waves (row pairs) per row-kernel workgroup
+constexpr int kStageRegs = 5;    // activation pieces per thread loaded ahead of the item prefetch
 
 __device__ __forceinline__ u32x4 ld_stream(const uint8_t* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ u32x2 ld8a4(const uint8_t* p) {
+  u32x2 v;
+  __builtin_memcpy(&v, __builtin_assume_aligned(p, 4), 8);
+  return v;
 }
 __device__ __forceinline__ u32x4 ld16a4(const uint8_t* p) {
   u32x4 v;
@@ -58,140 +68,8 @@ __device__ __forceinline__ float e4m3_group(uint32_t d, int g) {
                                                                              : e4m3_byte_f32<3>(d);
 }
 
-// ---- FP8 gate+up row kernel (bf16 x) -------------------------------------------------------------
-// ONE: the call has a single activation row (compile-time loop bound).
-template <int CH, bool ONE>
-__global__ void __launch_bounds__(256) fp8_gu_row(int M, int K, int N, const uint16_t* __restrict__ x,
-                                                 const uint8_t* __restrict__ wg, const float* __restrict__ sg,
-                                                 const uint8_t* __restrict__ wu, const float* __restrict__ su,
-                                                 float* __restrict__ act) {
-  const int C = K >> 4;
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= N) return;
-  u32x4 w[2][CH];
-#pragma unroll
-  for (int c = 0; c < CH; ++c) {
-    const int ch = lane + 64 * c;
-    if (ch < C) {
-      w[0][c] = ld_stream(wg + (size_t)row * K + 16 * ch);
-      w[1][c] = ld_stream(wu + (size_t)row * K + 16 * ch);
-    }
-  }
-  const float gsc = sg[row], usc = su[row];
-  const int Mloop = ONE ? 1 : M;
-  for (int m = 0; m < Mloop; ++m) {
-    const uint16_t* xm = x + (size_t)m * K;
-    u32x4 xr[CH][2];
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int ch = lane + 64 * c;
-      if (ch < C) {
-        xr[c][0] = *reinterpret_cast<const u32x4*>(xm + 16 * ch);
-        xr[c][1] = *reinterpret_cast<const u32x4*>(xm + 16 * ch + 8);
-      }
-    }
-    float a[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      if (lane + 64 * c < C) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const u32x4 v = w[t][c];
-          float p0 = a[t][0], p1 = a[t][1];
-          p0 = dot2_bf16(e4m3x2_bf16<false>(v.x), xr[c][0].x, p0);
-          p0 = dot2_bf16(e4m3x2_bf16<true>(v.x), xr[c][0].y, p0);
-          p1 = dot2_bf16(e4m3x2_bf16<false>(v.y), xr[c][0].z, p1);
-          p1 = dot2_bf16(e4m3x2_bf16<true>(v.y), xr[c][0].w, p1);
-          p0 = dot2_bf16(e4m3x2_bf16<false>(v.z), xr[c][1].x, p0);
-          p0 = dot2_bf16(e4m3x2_bf16<true>(v.z), xr[c][1].y, p0);
-          p1 = dot2_bf16(e4m3x2_bf16<false>(v.w), xr[c][1].z, p1);
-          p1 = dot2_bf16(e4m3x2_bf16<true>(v.w), xr[c][1].w, p1);
-          a[t][0] = p0;
-          a[t][1] = p1;
-        }
-      }
-    }
-    const float g = gsum<64>(a[0][0] + a[0][1]) * gsc;
-    const float u = gsum<64>(a[1][0] + a[1][1]) * usc;
-    if (lane == 0) act[(size_t)m * N + row] = silu_f32(g) * u;
-  }
-}
-
-// ---- NVFP4 gate+up row kernel (bf16 x in LDS, record r at r*144) -----------------------------------
-template <int NR, bool ONE>
-__global__ void __launch_bounds__(512) nv_gu_row(int M, int K, int N, const uint16_t* __restrict__ x,
-                                                const uint8_t* __restrict__ bg, float inv_g,
-                                                const uint8_t* __restrict__ bu, float inv_u, float* __restrict__ act) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  const int nrec = K >> 6;
-  const size_t rb = (size_t)nrec * 36;
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 8 + (threadIdx.x >> 6);
-  const bool on = row < N;
-  u32x4 A[2][NR], B[2][NR];
-  uint32_t Cw[2][NR];
-  if (on) {
-#pragma unroll
-    for (int t = 0; t < NR; ++t) {
-      const int r = lane + 64 * t;
-      if (r < nrec) {
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          const uint8_t* p = (mt ? bu : bg) + (size_t)row * rb + (size_t)r * 36;
-          A[mt][t] = ld16a4(p);
-          B[mt][t] = ld16a4(p + 16);
-          Cw[mt][t] = *reinterpret_cast<const uint32_t*>(p + 32);
-        }
-      }
-    }
-  }
-  const int Mloop = ONE ? 1 : M;
-  for (int m = 0; m < Mloop; ++m) {
-    if (m) __syncthreads();
-    const u32x4* xm = reinterpret_cast<const u32x4*>(x + (size_t)m * K);
-    for (int i = threadIdx.x; i < nrec * 8; i += blockDim.x)
-      *reinterpret_cast<u32x4*>(lds + (i >> 3) * 144 + (i & 7) * 16) = xm[i];
-    __syncthreads();
-    if (!on) continue;
-    float acc[2] = {0.f, 0.f};
-#pragma unroll
-    for (int t = 0; t < NR; ++t) {
-      const int r = lane + 64 * t;
-      if (r < nrec) {
-        const uint8_t* xl = lds + r * 144;
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          const uint32_t d = A[mt][t].x;
-          const uint32_t qs[8] = {A[mt][t].y, A[mt][t].z, A[mt][t].w, B[mt][t].x,
-                                  B[mt][t].y, B[mt][t].z, B[mt][t].w, Cw[mt][t]};
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const u32x4 x0 = *reinterpret_cast<const u32x4*>(xl + 32 * g);
-            const u32x4 x1 = *reinterpret_cast<const u32x4*>(xl + 32 * g + 16);
-            float part = 0.f;
-            part = dot2_bf16(e2m1x2_bf16<0>(qs[2 * g]), x0.x, part);
-            part = dot2_bf16(e2m1x2_bf16<1>(qs[2 * g]), x0.y, part);
-            part = dot2_bf16(e2m1x2_bf16<2>(qs[2 * g]), x0.z, part);
-            part = dot2_bf16(e2m1x2_bf16<3>(qs[2 * g]), x0.w, part);
-            part = dot2_bf16(e2m1x2_bf16<0>(qs[2 * g + 1]), x1.x, part);
-            part = dot2_bf16(e2m1x2_bf16<1>(qs[2 * g + 1]), x1.y, part);
-            part = dot2_bf16(e2m1x2_bf16<2>(qs[2 * g + 1]), x1.z, part);
-            part = dot2_bf16(e2m1x2_bf16<3>(qs[2 * g + 1]), x1.w, part);
-            acc[mt] = fmaf(part, e4m3_group(d, g), acc[mt]);
-          }
-        }
-      }
-    }
-    const float gv = gsum<64>(acc[0]) * inv_g;
-    const float uv = gsum<64>(acc[1]) * inv_u;
-    if (lane == 0) act[(size_t)m * N + row] = silu_f32(gv) * uv;
-  }
-}
-
-// ---- item kernels ---------------------------------------------------------------------------------
-// Activation row m staged into LDS piece-major: piece q (16 bytes) of unit u at (q * U + u) * 16, where a
-// unit is an FP8 chunk (16 codes) or an NVFP4 record (64 codes) and PQ pieces make one unit.
+// An activation row staged into LDS piece-major: piece q (16 bytes) of unit u at (q * U + u) * 16, where
+// a unit holds 16 activations and PQ pieces make one unit, so consecutive lanes read consecutive pieces.
 template <typename XT, int UNIT>
 __device__ __forceinline__ void stage_units(uint8_t* lds, const XT* __restrict__ xm, int U) {
   constexpr int PQ = UNIT * (int)sizeof(XT) / 16;
@@ -202,6 +80,165 @@ __device__ __forceinline__ void stage_units(uint8_t* lds, const XT* __restrict__
   }
 }
 
+
+// The same staging split in two so that the activation loads can be issued before a weight prefetch
+// (per-wave loads complete in order, so staging issued after the prefetch would wait for all of it);
+// used by the single-row item kernels (the multi-row ones would keep the registers live across m):
+// issue() loads up to kStageRegs pieces per thread into registers, finish() writes them to LDS and
+// stages any remainder with a plain loop.
+template <typename XT>
+struct StageRegs {
+  u32x4 v[kStageRegs];
+  __device__ __forceinline__ void issue(const XT* __restrict__ xm, int U) {
+    constexpr int PQ = 16 * (int)sizeof(XT) / 16;
+    const u32x4* src = reinterpret_cast<const u32x4*>(xm);
+#pragma unroll
+    for (int j = 0; j < kStageRegs; ++j) {
+      const int i = threadIdx.x + j * (int)blockDim.x;
+      if (i < U * PQ) v[j] = src[i];
+    }
+  }
+  __device__ __forceinline__ void finish(uint8_t* lds, const XT* __restrict__ xm, int U) {
+    constexpr int PQ = 16 * (int)sizeof(XT) / 16;
+#pragma unroll
+    for (int j = 0; j < kStageRegs; ++j) {
+      const int i = threadIdx.x + j * (int)blockDim.x;
+      if (i < U * PQ) {
+        const int u = i / PQ, q = i - u * PQ;
+        *reinterpret_cast<u32x4*>(lds + ((size_t)q * U + u) * 16) = v[j];
+      }
+    }
+    const u32x4* src = reinterpret_cast<const u32x4*>(xm);
+    for (int i = threadIdx.x + kStageRegs * (int)blockDim.x; i < U * PQ; i += blockDim.x) {
+      const int u = i / PQ, q = i - u * PQ;
+      *reinterpret_cast<u32x4*>(lds + ((size_t)q * U + u) * 16) = src[i];
+    }
+  }
+};
+
+// ---- FP8 gate+up row kernel (bf16 x) -------------------------------------------------------------
+// kRowWaves waves per workgroup, one row pair each; the x row is staged once per workgroup into LDS
+// (piece q of chunk c at (q * C + c) * 16) after the weight loads are issued, and read chunk by chunk.
+// ONE: the call has a single activation row (compile-time loop bound).
+template <int CH, bool ONE>
+__global__ void __launch_bounds__(64 * kRowWaves) fp8_gu_row(int M, int K, int N, const uint16_t* __restrict__ x,
+                                                          const uint8_t* __restrict__ wg, const float* __restrict__ sg,
+                                                          const uint8_t* __restrict__ wu, const float* __restrict__ su,
+                                                          float* __restrict__ act) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int C = K >> 4;
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * kRowWaves + (threadIdx.x >> 6);
+  const int rl = min(row, N - 1);   // rows past N compute on row N-1 and store nothing
+  u32x4 w[2][CH];
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int ch = min(lane + 64 * c, C - 1);
+    w[0][c] = ld_stream(wg + (size_t)rl * K + 16 * ch);
+    w[1][c] = ld_stream(wu + (size_t)rl * K + 16 * ch);
+  }
+  const int Mloop = ONE ? 1 : M;
+  for (int m = 0; m < Mloop; ++m) {
+    if (m) __syncthreads();
+    stage_units<uint16_t, 16>(lds, x + (size_t)m * K, C);
+    __syncthreads();
+    float a[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int ch = lane + 64 * c;
+      if (ch < C) {
+        const u32x4 x0 = *reinterpret_cast<const u32x4*>(lds + (size_t)ch * 16);
+        const u32x4 x1 = *reinterpret_cast<const u32x4*>(lds + ((size_t)C + ch) * 16);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const u32x4 v = w[t][c];
+          float p0 = a[t][0], p1 = a[t][1];
+          p0 = dot2_bf16(e4m3x2_bf16<false>(v.x), x0.x, p0);
+          p0 = dot2_bf16(e4m3x2_bf16<true>(v.x), x0.y, p0);
+          p1 = dot2_bf16(e4m3x2_bf16<false>(v.y), x0.z, p1);
+          p1 = dot2_bf16(e4m3x2_bf16<true>(v.y), x0.w, p1);
+          p0 = dot2_bf16(e4m3x2_bf16<false>(v.z), x1.x, p0);
+          p0 = dot2_bf16(e4m3x2_bf16<true>(v.z), x1.y, p0);
+          p1 = dot2_bf16(e4m3x2_bf16<false>(v.w), x1.z, p1);
+          p1 = dot2_bf16(e4m3x2_bf16<true>(v.w), x1.w, p1);
+          a[t][0] = p0;
+          a[t][1] = p1;
+        }
+      }
+    }
+    if (row < N) {
+      const float g = gsum<64>(a[0][0] + a[0][1]) * sg[row];
+      const float u = gsum<64>(a[1][0] + a[1][1]) * su[row];
+      if (lane == 0) act[(size_t)m * N + row] = silu_f32(g) * u;
+    }
+  }
+}
+
+// ---- NVFP4 gate+up row kernel (bf16 x), group mapping ---------------------------------------------
+// Unit of work per lane: one 16-weight group = 8 nibble bytes (qs[8q..8q+7] of its record) plus the
+// record's scale byte d[q].  Lane l owns groups l, l+64, ... of its row; the four lanes 4j..4j+3 read
+// record j's 32 nibble bytes contiguously, so a wave's loads cover the row's records without gaps.
+// Workgroup shape and x staging as in the FP8 row kernel.
+template <int CH, bool ONE>
+__global__ void __launch_bounds__(64 * kRowWaves) nv_gu_grp(int M, int K, int N, const uint16_t* __restrict__ x,
+                                                         const uint8_t* __restrict__ bg, float inv_g,
+                                                         const uint8_t* __restrict__ bu, float inv_u,
+                                                         float* __restrict__ act) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int G = K >> 4;
+  const size_t rb = (size_t)(K >> 6) * 36;
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * kRowWaves + (threadIdx.x >> 6);
+  const int rl = min(row, N - 1);   // rows past N compute on row N-1 and store nothing
+  u32x2 q[2][CH];
+  uint32_t sc[2][CH];
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int g = min(lane + 64 * c, G - 1);   // clamped: in bounds, never accumulated
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const uint8_t* p = (mt ? bu : bg) + (size_t)rl * rb + (size_t)(g >> 2) * 36;
+      q[mt][c] = ld8a4(p + 4 + 8 * (g & 3));
+      sc[mt][c] = p[g & 3];
+    }
+  }
+  const int Mloop = ONE ? 1 : M;
+  for (int m = 0; m < Mloop; ++m) {
+    if (m) __syncthreads();
+    stage_units<uint16_t, 16>(lds, x + (size_t)m * K, G);
+    __syncthreads();
+    float acc[2] = {0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int g = lane + 64 * c;
+      if (g < G) {
+        const u32x4 x0 = *reinterpret_cast<const u32x4*>(lds + (size_t)g * 16);
+        const u32x4 x1 = *reinterpret_cast<const u32x4*>(lds + ((size_t)G + g) * 16);
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          const u32x2 w = q[mt][c];
+          float pt = 0.f;
+          pt = dot2_bf16(e2m1x2_bf16<0>(w.x), x0.x, pt);
+          pt = dot2_bf16(e2m1x2_bf16<1>(w.x), x0.y, pt);
+          pt = dot2_bf16(e2m1x2_bf16<2>(w.x), x0.z, pt);
+          pt = dot2_bf16(e2m1x2_bf16<3>(w.x), x0.w, pt);
+          pt = dot2_bf16(e2m1x2_bf16<0>(w.y), x1.x, pt);
+          pt = dot2_bf16(e2m1x2_bf16<1>(w.y), x1.y, pt);
+          pt = dot2_bf16(e2m1x2_bf16<2>(w.y), x1.z, pt);
+          pt = dot2_bf16(e2m1x2_bf16<3>(w.y), x1.w, pt);
+          acc[mt] = fmaf(pt, e4m3_byte_f32<0>(sc[mt][c]), acc[mt]);
+        }
+      }
+    }
+    if (row < N) {
+      const float gv = gsum<64>(acc[0]) * inv_g;
+      const float uv = gsum<64>(acc[1]) * inv_u;
+      if (lane == 0) act[(size_t)m * N + row] = silu_f32(gv) * uv;
+    }
+  }
+}
+
+// ---- item kernels ---------------------------------------------------------------------------------
 // Item cursor: item it = g * T + t advanced by NW per step without divisions.
 struct ItemCursor {
   int g, t;
@@ -253,9 +290,17 @@ __global__ void __launch_bounds__(64 * kItemWaves, 8) fp8_lin_items(int M, int K
       ++lk;
       lc.step(NW, T);
     };
+    if constexpr (ONE) {
+      StageRegs<XT> sr;
+      sr.issue(xa, C);
 #pragma unroll
-    for (int b = 0; b < D; ++b) load(b);
-    stage_units<XT, 16>(lds, xa + (size_t)m * K, C);
+      for (int b = 0; b < D; ++b) load(b);
+      sr.finish(lds, xa, C);
+    } else {
+#pragma unroll
+      for (int b = 0; b < D; ++b) load(b);
+      stage_units<XT, 16>(lds, xa + (size_t)m * K, C);
+    }
     __syncthreads();
     float acc[R][2];
 #pragma unroll
@@ -338,52 +383,67 @@ __global__ void __launch_bounds__(64 * kItemWaves, 8) fp8_lin_items(int M, int K
   }
 }
 
-// NVFP4 single linear: y[m, n] = inv * sum_k xa[m, k] dq(blk[n, k]).
+// NVFP4 single linear: y[m, n] = inv * sum_k xa[m, k] dq(blk[n, k]).  Same item schedule as the FP8
+// kernel, with the 16-weight group (8 nibble bytes + its scale byte) as the per-lane unit.
 template <typename XT, bool ONE>
-__global__ void __launch_bounds__(64 * kItemWaves, 8) nv_lin_items(int M, int K, int N, const XT* __restrict__ xa,
-                                                                const uint8_t* __restrict__ blk, float inv,
-                                                                float* __restrict__ y) {
-  constexpr int D = kItemDepth, NW = kItemWaves, RB = kItemRows;
+__global__ void __launch_bounds__(64 * kItemWaves, 8) nv_lin_grp(int M, int K, int N, const XT* __restrict__ xa,
+                                                              const uint8_t* __restrict__ blk, float inv,
+                                                              float* __restrict__ y) {
+  constexpr int R = 2, D = kItemDepth, NW = kItemWaves, RB = kItemRows;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   __shared__ float part[NW][RB];
-  const int nrec = K >> 6, T = (nrec + 63) >> 6;
-  const size_t rb = (size_t)nrec * 36;
+  const int G = K >> 4, T = (G + 63) >> 6;
+  const size_t rb = (size_t)(K >> 6) * 36;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int rbase = blockIdx.x * RB;
-  const int NI = RB * T;
+  const int NI = (RB / R) * T;
   const int nk = NI > wv ? (NI - wv + NW - 1) / NW : 0;
   const int Mloop = ONE ? 1 : M;
   for (int m = 0; m < Mloop; ++m) {
     if (m) __syncthreads();
     for (int i = threadIdx.x; i < NW * RB; i += blockDim.x) (&part[0][0])[i] = 0.f;
-    u32x4 A[D], B[D];
-    uint32_t Cw[D];
+    u32x2 qb[D][R];
+    uint32_t sb[D][R];
     ItemCursor lc;
     lc.init(wv, T);
     int lk = 0;
     auto load = [&](int b) {
       if (lk < nk) {
-        // Clamped to the last record / row: in bounds, and never accumulated or stored.
-        const int r = min(lane + 64 * lc.t, nrec - 1), n = min(rbase + lc.g, N - 1);
-        const uint8_t* p = blk + (size_t)n * rb + (size_t)r * 36;
-        A[b] = ld16a4(p);
-        B[b] = ld16a4(p + 16);
-        Cw[b] = *reinterpret_cast<const uint32_t*>(p + 32);
+        // Clamped to the last group / row: in bounds, and never accumulated or stored.
+        const int g = min(lane + 64 * lc.t, G - 1);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const int n = min(rbase + lc.g * R + r, N - 1);
+          const uint8_t* p = blk + (size_t)n * rb + (size_t)(g >> 2) * 36;
+          qb[b][r] = ld8a4(p + 4 + 8 * (g & 3));
+          sb[b][r] = p[g & 3];
+        }
       }
       ++lk;
       lc.step(NW, T);
     };
+    if constexpr (ONE) {
+      StageRegs<XT> sr;
+      sr.issue(xa, G);
 #pragma unroll
-    for (int b = 0; b < D; ++b) load(b);
-    stage_units<XT, 64>(lds, xa + (size_t)m * K, nrec);
+      for (int b = 0; b < D; ++b) load(b);
+      sr.finish(lds, xa, G);
+    } else {
+#pragma unroll
+      for (int b = 0; b < D; ++b) load(b);
+      stage_units<XT, 16>(lds, xa + (size_t)m * K, G);
+    }
     __syncthreads();
-    float acc = 0.f;
+    float acc[R] = {0.f, 0.f};
     int cur = -1;
     auto flush = [&]() {
       if (cur < 0) return;
-      const float v = gsum<64>(acc);
-      acc = 0.f;
-      if (lane == 0) part[wv][cur] = v;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const float v = gsum<64>(acc[r]);
+        acc[r] = 0.f;
+        if (lane == 0) part[wv][cur * R + r] = v;
+      }
     };
     ItemCursor cc;
     cc.init(wv, T);
@@ -392,50 +452,57 @@ __global__ void __launch_bounds__(64 * kItemWaves, 8) nv_lin_items(int M, int K,
       for (int b = 0; b < D; ++b) {
         const int k = k0 + b;
         if (k < nk) {
-          const int g = cc.g, r = lane + 64 * cc.t;
+          const int gi = cc.g, g = lane + 64 * cc.t;
           cc.step(NW, T);
-          if (g != cur) {
+          if (gi != cur) {
             flush();
-            cur = g;
+            cur = gi;
           }
-          if (r < nrec) {
-            const uint32_t d = A[b].x;
-            const uint32_t qs[8] = {A[b].y, A[b].z, A[b].w, B[b].x, B[b].y, B[b].z, B[b].w, Cw[b]};
+          if (g < G) {
+            if constexpr (sizeof(XT) == 4) {
+              f32x4 xv[4];
 #pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
-              float pt = 0.f;
-              if constexpr (sizeof(XT) == 4) {
+              for (int qq = 0; qq < 4; ++qq) xv[qq] = *reinterpret_cast<const f32x4*>(lds + ((size_t)qq * G + g) * 16);
+#pragma unroll
+              for (int r = 0; r < R; ++r) {
+                const u32x2 w = qb[b][r];
+                float pt = 0.f;
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
-                  const f32x4 xa0 = *reinterpret_cast<const f32x4*>(lds + ((size_t)(4 * gq + 2 * h) * nrec + r) * 16);
-                  const f32x4 xa1 = *reinterpret_cast<const f32x4*>(lds + ((size_t)(4 * gq + 2 * h + 1) * nrec + r) * 16);
-                  const uint32_t wq = qs[2 * gq + h];
-                  f32x2 e = e2m1x2_f32<0>(wq);
-                  pt = fmaf(xa0.x, e.x, pt);
-                  pt = fmaf(xa0.y, e.y, pt);
-                  e = e2m1x2_f32<1>(wq);
-                  pt = fmaf(xa0.z, e.x, pt);
-                  pt = fmaf(xa0.w, e.y, pt);
-                  e = e2m1x2_f32<2>(wq);
-                  pt = fmaf(xa1.x, e.x, pt);
-                  pt = fmaf(xa1.y, e.y, pt);
-                  e = e2m1x2_f32<3>(wq);
-                  pt = fmaf(xa1.z, e.x, pt);
-                  pt = fmaf(xa1.w, e.y, pt);
+                  const uint32_t wd = h ? w.y : w.x;
+                  const f32x4 a0 = xv[2 * h], a1 = xv[2 * h + 1];
+                  f32x2 e = e2m1x2_f32<0>(wd);
+                  pt = fmaf(a0.x, e.x, pt);
+                  pt = fmaf(a0.y, e.y, pt);
+                  e = e2m1x2_f32<1>(wd);
+                  pt = fmaf(a0.z, e.x, pt);
+                  pt = fmaf(a0.w, e.y, pt);
+                  e = e2m1x2_f32<2>(wd);
+                  pt = fmaf(a1.x, e.x, pt);
+                  pt = fmaf(a1.y, e.y, pt);
+                  e = e2m1x2_f32<3>(wd);
+                  pt = fmaf(a1.z, e.x, pt);
+                  pt = fmaf(a1.w, e.y, pt);
                 }
-              } else {
-                const u32x4 x0 = *reinterpret_cast<const u32x4*>(lds + ((size_t)(2 * gq) * nrec + r) * 16);
-                const u32x4 x1 = *reinterpret_cast<const u32x4*>(lds + ((size_t)(2 * gq + 1) * nrec + r) * 16);
-                pt = dot2_bf16(e2m1x2_bf16<0>(qs[2 * gq]), x0.x, pt);
-                pt = dot2_bf16(e2m1x2_bf16<1>(qs[2 * gq]), x0.y, pt);
-                pt = dot2_bf16(e2m1x2_bf16<2>(qs[2 * gq]), x0.z, pt);
-                pt = dot2_bf16(e2m1x2_bf16<3>(qs[2 * gq]), x0.w, pt);
-                pt = dot2_bf16(e2m1x2_bf16<0>(qs[2 * gq + 1]), x1.x, pt);
-                pt = dot2_bf16(e2m1x2_bf16<1>(qs[2 * gq + 1]), x1.y, pt);
-                pt = dot2_bf16(e2m1x2_bf16<2>(qs[2 * gq + 1]), x1.z, pt);
-                pt = dot2_bf16(e2m1x2_bf16<3>(qs[2 * gq + 1]), x1.w, pt);
+                acc[r] = fmaf(pt, e4m3_byte_f32<0>(sb[b][r]), acc[r]);
               }
-              acc = fmaf(pt, e4m3_group(d, gq), acc);
+            } else {
+              const u32x4 x0 = *reinterpret_cast<const u32x4*>(lds + ((size_t)0 * G + g) * 16);
+              const u32x4 x1 = *reinterpret_cast<const u32x4*>(lds + ((size_t)1 * G + g) * 16);
+#pragma unroll
+              for (int r = 0; r < R; ++r) {
+                const u32x2 w = qb[b][r];
+                float pt = 0.f;
+                pt = dot2_bf16(e2m1x2_bf16<0>(w.x), x0.x, pt);
+                pt = dot2_bf16(e2m1x2_bf16<1>(w.x), x0.y, pt);
+                pt = dot2_bf16(e2m1x2_bf16<2>(w.x), x0.z, pt);
+                pt = dot2_bf16(e2m1x2_bf16<3>(w.x), x0.w, pt);
+                pt = dot2_bf16(e2m1x2_bf16<0>(w.y), x1.x, pt);
+                pt = dot2_bf16(e2m1x2_bf16<1>(w.y), x1.y, pt);
+                pt = dot2_bf16(e2m1x2_bf16<2>(w.y), x1.z, pt);
+                pt = dot2_bf16(e2m1x2_bf16<3>(w.y), x1.w, pt);
+                acc[r] = fmaf(pt, e4m3_byte_f32<0>(sb[b][r]), acc[r]);
+              }
             }
           }
           load(b);
@@ -475,7 +542,7 @@ bool fast_gemv_fp8_ok(int K, XType xt, bool gu) {
 
 bool fast_gemv_nvfp4_ok(int K, XType xt, bool gu) {
   if (K % 64) return false;
-  if (gu) return xt == X_BF16 && (K / 64 + 63) / 64 <= 4;
+  if (gu) return xt == X_BF16 && (K / 16 + 63) / 64 <= 8;
   return (size_t)K * (xt == X_F32 ? 4 : 2) <= kMaxItemLds;
 }
 
@@ -483,13 +550,14 @@ hipError_t launch_fast_fp8(int M, int K, int N, const void* x, XType xt, const u
                            const uint8_t* w1, const float* s1, float* y, hipStream_t st) {
   if (w1 != nullptr) {
     const int CH = (K / 16 + 63) / 64;
-    const dim3 grid((N + 3) / 4), block(256);
+    const dim3 grid((N + kRowWaves - 1) / kRowWaves), block(64 * kRowWaves);
+    const size_t lds = (size_t)K * 2;
     const uint16_t* xb = reinterpret_cast<const uint16_t*>(x);
     switch (CH) {
-#define WQ_CASE(n)                                                                                       \
-  case n:                                                                                                \
-    if (M == 1) hipLaunchKernelGGL((fp8_gu_row<n, true>), grid, block, 0, st, M, K, N, xb, w0, s0, w1, s1, y); \
-    else hipLaunchKernelGGL((fp8_gu_row<n, false>), grid, block, 0, st, M, K, N, xb, w0, s0, w1, s1, y);      \
+#define WQ_CASE(n)                                                                                         \
+  case n:                                                                                                  \
+    if (M == 1) hipLaunchKernelGGL((fp8_gu_row<n, true>), grid, block, lds, st, M, K, N, xb, w0, s0, w1, s1, y); \
+    else hipLaunchKernelGGL((fp8_gu_row<n, false>), grid, block, lds, st, M, K, N, xb, w0, s0, w1, s1, y);      \
     break;
       WQ_CASE(1) WQ_CASE(2) WQ_CASE(3) WQ_CASE(4) WQ_CASE(5) WQ_CASE(6) WQ_CASE(7) WQ_CASE(8)
 #undef WQ_CASE
@@ -518,17 +586,17 @@ hipError_t launch_fast_fp8(int M, int K, int N, const void* x, XType xt, const u
 hipError_t launch_fast_nvfp4(int M, int K, int N, const void* x, XType xt, const uint8_t* b0, float inv0,
                              const uint8_t* b1, float inv1, float* y, hipStream_t st) {
   if (b1 != nullptr) {
-    const int NR = (K / 64 + 63) / 64;
-    const size_t lds = (size_t)(K / 64) * 144;
-    const dim3 grid((N + 7) / 8), block(512);
+    const int CH = (K / 16 + 63) / 64;
+    const dim3 grid((N + kRowWaves - 1) / kRowWaves), block(64 * kRowWaves);
+    const size_t lds = (size_t)K * 2;
     const uint16_t* xb = reinterpret_cast<const uint16_t*>(x);
-    switch (NR) {
-#define WQ_CASE(n)                                                                                          \
-  case n:                                                                                                   \
-    if (M == 1) hipLaunchKernelGGL((nv_gu_row<n, true>), grid, block, lds, st, M, K, N, xb, b0, inv0, b1, inv1, y); \
-    else hipLaunchKernelGGL((nv_gu_row<n, false>), grid, block, lds, st, M, K, N, xb, b0, inv0, b1, inv1, y);      \
+    switch (CH) {
+#define WQ_CASE(n)                                                                                           \
+  case n:                                                                                                    \
+    if (M == 1) hipLaunchKernelGGL((nv_gu_grp<n, true>), grid, block, lds, st, M, K, N, xb, b0, inv0, b1, inv1, y); \
+    else hipLaunchKernelGGL((nv_gu_grp<n, false>), grid, block, lds, st, M, K, N, xb, b0, inv0, b1, inv1, y);      \
     break;
-      WQ_CASE(1) WQ_CASE(2) WQ_CASE(3) WQ_CASE(4)
+      WQ_CASE(1) WQ_CASE(2) WQ_CASE(3) WQ_CASE(4) WQ_CASE(5) WQ_CASE(6) WQ_CASE(7) WQ_CASE(8)
 #undef WQ_CASE
       default: return hipErrorInvalidValue;
     }
@@ -538,8 +606,8 @@ hipError_t launch_fast_nvfp4(int M, int K, int N, const void* x, XType xt, const
   const dim3 grid((N + kItemRows - 1) / kItemRows), block(64 * kItemWaves);
 #define WQ_LAUNCH(T, O)                                                                                      \
   do {                                                                                                       \
-    if (!lds_ok(nv_lin_items<T, O>, lds)) return hipErrorInvalidValue;                                       \
-    hipLaunchKernelGGL((nv_lin_items<T, O>), grid, block, lds, st, M, K, N, reinterpret_cast<const T*>(x), b0, inv0, y); \
+    if (!lds_ok(nv_lin_grp<T, O>, lds)) return hipErrorInvalidValue;                                       \
+    hipLaunchKernelGGL((nv_lin_grp<T, O>), grid, block, lds, st, M, K, N, reinterpret_cast<const T*>(x), b0, inv0, y); \
   } while (0)
   if (xt == X_F32) {
     if (M == 1) WQ_LAUNCH(float, true);
