@@ -7,8 +7,9 @@
 //
 // Two kernel shapes, chosen from measurements of the 5120 x 17408 decode:
 //  * row kernels (gate+up): one wave per output row pair (gate row n, up row n); every weight load of the
-//    pair is issued at once (2 x 5 KB for FP8 at K=5120), then the workgroup stages the activation row in
-//    LDS (one copy per 8 row pairs instead of one per wave); occupancy 8 waves/SIMD.  The weights stay in
+//    pair is issued at once (2 x 5 KB for FP8 at K=5120), right after the loads of the workgroup's x
+//    row, which is staged in LDS (one copy per 8 row pairs instead of one per wave); occupancy 8
+//    waves/SIMD.  The weights stay in
 //    registers while the m rows of a multi-row call are processed one by one.
 //  * item kernels (down projection / single linear): a 16-wave workgroup owns RB output rows; the
 //    activation row is staged once into LDS; the (row pair, K slot) work items -- a K slot is one unit per
@@ -43,6 +44,7 @@ constexpr int kItemRows = 20;    // output rows per item-kernel workgroup
 constexpr int kItemDepth = 2;    // loads in flight per wave (items)
 constexpr int kRowWaves = 8;     // waves (row pairs) per row-kernel workgroup
 constexpr int kStageRegs = 5;    // activation pieces per thread loaded ahead of the item prefetch
+constexpr int kRowStageRegs = 2; // x pieces per thread loaded ahead of the row-kernel weights (K <= 8192)
 
 __device__ __forceinline__ u32x4 ld_stream(const uint8_t* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
@@ -83,17 +85,17 @@ __device__ __forceinline__ void stage_units(uint8_t* lds, const XT* __restrict__
 
 // The same staging split in two so that the activation loads can be issued before a weight prefetch
 // (per-wave loads complete in order, so staging issued after the prefetch would wait for all of it);
-// used by the single-row item kernels (the multi-row ones would keep the registers live across m):
-// issue() loads up to kStageRegs pieces per thread into registers, finish() writes them to LDS and
-// stages any remainder with a plain loop.
-template <typename XT>
+// used by the single-row kernels (the multi-row ones would keep the registers live across m):
+// issue() loads up to SPT pieces per thread into registers, finish() writes them to LDS and stages any
+// remainder with a plain loop.
+template <typename XT, int SPT>
 struct StageRegs {
-  u32x4 v[kStageRegs];
+  u32x4 v[SPT];
   __device__ __forceinline__ void issue(const XT* __restrict__ xm, int U) {
     constexpr int PQ = 16 * (int)sizeof(XT) / 16;
     const u32x4* src = reinterpret_cast<const u32x4*>(xm);
 #pragma unroll
-    for (int j = 0; j < kStageRegs; ++j) {
+    for (int j = 0; j < SPT; ++j) {
       const int i = threadIdx.x + j * (int)blockDim.x;
       if (i < U * PQ) v[j] = src[i];
     }
@@ -101,7 +103,7 @@ struct StageRegs {
   __device__ __forceinline__ void finish(uint8_t* lds, const XT* __restrict__ xm, int U) {
     constexpr int PQ = 16 * (int)sizeof(XT) / 16;
 #pragma unroll
-    for (int j = 0; j < kStageRegs; ++j) {
+    for (int j = 0; j < SPT; ++j) {
       const int i = threadIdx.x + j * (int)blockDim.x;
       if (i < U * PQ) {
         const int u = i / PQ, q = i - u * PQ;
@@ -109,7 +111,7 @@ struct StageRegs {
       }
     }
     const u32x4* src = reinterpret_cast<const u32x4*>(xm);
-    for (int i = threadIdx.x + kStageRegs * (int)blockDim.x; i < U * PQ; i += blockDim.x) {
+    for (int i = threadIdx.x + SPT * (int)blockDim.x; i < U * PQ; i += blockDim.x) {
       const int u = i / PQ, q = i - u * PQ;
       *reinterpret_cast<u32x4*>(lds + ((size_t)q * U + u) * 16) = src[i];
     }
@@ -130,6 +132,10 @@ __global__ void __launch_bounds__(64 * kRowWaves) fp8_gu_row(int M, int K, int N
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * kRowWaves + (threadIdx.x >> 6);
   const int rl = min(row, N - 1);   // rows past N compute on row N-1 and store nothing
+  // Single-row calls issue the x loads before the weight loads: loads of a wave complete in order, so
+  // the workgroup barrier then waits only for x, not for every wave's weights.
+  StageRegs<uint16_t, kRowStageRegs> sr;
+  if constexpr (ONE) sr.issue(x, C);
   u32x4 w[2][CH];
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
@@ -139,8 +145,12 @@ __global__ void __launch_bounds__(64 * kRowWaves) fp8_gu_row(int M, int K, int N
   }
   const int Mloop = ONE ? 1 : M;
   for (int m = 0; m < Mloop; ++m) {
-    if (m) __syncthreads();
-    stage_units<uint16_t, 16>(lds, x + (size_t)m * K, C);
+    if constexpr (ONE) {
+      sr.finish(lds, x, C);
+    } else {
+      if (m) __syncthreads();
+      stage_units<uint16_t, 16>(lds, x + (size_t)m * K, C);
+    }
     __syncthreads();
     float a[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
 #pragma unroll
@@ -190,6 +200,10 @@ __global__ void __launch_bounds__(64 * kRowWaves) nv_gu_grp(int M, int K, int N,
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * kRowWaves + (threadIdx.x >> 6);
   const int rl = min(row, N - 1);   // rows past N compute on row N-1 and store nothing
+  // Single-row calls issue the x loads before the weight loads: loads of a wave complete in order, so
+  // the workgroup barrier then waits only for x, not for every wave's weights.
+  StageRegs<uint16_t, kRowStageRegs> sr;
+  if constexpr (ONE) sr.issue(x, G);
   u32x2 q[2][CH];
   uint32_t sc[2][CH];
 #pragma unroll
@@ -204,8 +218,12 @@ __global__ void __launch_bounds__(64 * kRowWaves) nv_gu_grp(int M, int K, int N,
   }
   const int Mloop = ONE ? 1 : M;
   for (int m = 0; m < Mloop; ++m) {
-    if (m) __syncthreads();
-    stage_units<uint16_t, 16>(lds, x + (size_t)m * K, G);
+    if constexpr (ONE) {
+      sr.finish(lds, x, G);
+    } else {
+      if (m) __syncthreads();
+      stage_units<uint16_t, 16>(lds, x + (size_t)m * K, G);
+    }
     __syncthreads();
     float acc[2] = {0.f, 0.f};
 #pragma unroll
@@ -265,10 +283,12 @@ __global__ void __launch_bounds__(64 * kItemWaves, 8) fp8_lin_items(int M, int K
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   __shared__ float part[NW][RB];
   const int C = K >> 4, T = (C + 63) >> 6;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform: cursor in SGPRs
   const int rbase = blockIdx.x * RB;
   const int NI = (RB / R) * T;
   const int nk = NI > wv ? (NI - wv + NW - 1) / NW : 0;
+  const uint32_t lane_off = 16u * lane, max_off = 16u * (C - 1);
   const int Mloop = ONE ? 1 : M;
   for (int m = 0; m < Mloop; ++m) {
     if (m) __syncthreads();
@@ -279,19 +299,20 @@ __global__ void __launch_bounds__(64 * kItemWaves, 8) fp8_lin_items(int M, int K
     int lk = 0;
     auto load = [&](int b) {
       if (lk < nk) {
-        // Clamped to the last chunk / row: in bounds, and never accumulated or stored.
-        const int c = min(lane + 64 * lc.t, C - 1);
+        // Row base is wave-uniform; the lane offset is clamped to the last chunk and rows to the last
+        // row: in bounds, and never accumulated or stored.
+        const uint32_t off = min(1024u * lc.t + lane_off, max_off);
 #pragma unroll
         for (int r = 0; r < R; ++r) {
           const int n = min(rbase + lc.g * R + r, N - 1);
-          buf[b][r] = ld_stream(w + (size_t)n * K + 16 * c);
+          buf[b][r] = ld_stream(w + (size_t)n * K + off);
         }
       }
       ++lk;
       lc.step(NW, T);
     };
     if constexpr (ONE) {
-      StageRegs<XT> sr;
+      StageRegs<XT, kStageRegs> sr;
       sr.issue(xa, C);
 #pragma unroll
       for (int b = 0; b < D; ++b) load(b);
@@ -394,10 +415,15 @@ __global__ void __launch_bounds__(64 * kItemWaves, 8) nv_lin_grp(int M, int K, i
   __shared__ float part[NW][RB];
   const int G = K >> 4, T = (G + 63) >> 6;
   const size_t rb = (size_t)(K >> 6) * 36;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform: cursor in SGPRs
   const int rbase = blockIdx.x * RB;
   const int NI = (RB / R) * T;
   const int nk = NI > wv ? (NI - wv + NW - 1) / NW : 0;
+  // Byte offsets inside a row of group g = 64 t + lane: its nibbles at (g/4)*36 + 4 + 8*(g%4) and its
+  // scale at (g/4)*36 + g%4; both increase with g, so clamping to group G-1 is one min each.
+  const uint32_t q_lane = (lane >> 2) * 36u + 4u + 8u * (lane & 3), s_lane = (lane >> 2) * 36u + (lane & 3);
+  const uint32_t q_max = ((G - 1) >> 2) * 36u + 4u + 8u * ((G - 1) & 3), s_max = ((G - 1) >> 2) * 36u + ((G - 1) & 3);
   const int Mloop = ONE ? 1 : M;
   for (int m = 0; m < Mloop; ++m) {
     if (m) __syncthreads();
@@ -409,21 +435,22 @@ __global__ void __launch_bounds__(64 * kItemWaves, 8) nv_lin_grp(int M, int K, i
     int lk = 0;
     auto load = [&](int b) {
       if (lk < nk) {
-        // Clamped to the last group / row: in bounds, and never accumulated or stored.
-        const int g = min(lane + 64 * lc.t, G - 1);
+        // Row base is wave-uniform; offsets clamped to the last group and rows to the last row: in
+        // bounds, and never accumulated or stored.
+        const uint32_t qo = min(576u * lc.t + q_lane, q_max), so = min(576u * lc.t + s_lane, s_max);
 #pragma unroll
         for (int r = 0; r < R; ++r) {
           const int n = min(rbase + lc.g * R + r, N - 1);
-          const uint8_t* p = blk + (size_t)n * rb + (size_t)(g >> 2) * 36;
-          qb[b][r] = ld8a4(p + 4 + 8 * (g & 3));
-          sb[b][r] = p[g & 3];
+          const uint8_t* p = blk + (size_t)n * rb;
+          qb[b][r] = ld8a4(p + qo);
+          sb[b][r] = p[so];
         }
       }
       ++lk;
       lc.step(NW, T);
     };
     if constexpr (ONE) {
-      StageRegs<XT> sr;
+      StageRegs<XT, kStageRegs> sr;
       sr.issue(xa, G);
 #pragma unroll
       for (int b = 0; b < D; ++b) load(b);
