@@ -166,7 +166,9 @@ size_t awq_bank_bytes(int64_t E, int64_t N, int64_t K, int meta_layout);
  *   w2_bank   E experts of [H, I]
  *   act       [topk, I]  float16 out (also the W13 stage's result)
  *   out       [H]        float16 out
- * Shapes: E >= 1, 1 <= topk <= WQ_MOE_MAX_TOPK, H and I positive multiples of 32.
+ * Shapes: E >= 1, 1 <= topk <= WQ_MOE_MAX_TOPK, H and I positive multiples of 32,
+ * H, I <= 16384, (H/32)*80 <= 65536 and topk*((I/32)*80 + 128) <= 65536 (the staged
+ * activations must fit LDS); otherwise WQ_EINVAL.
  * Sums are float32; the order inside each dot product is fixed.
  */
 int moe_awq_m1_run(int64_t E, int64_t topk, int64_t H, int64_t I,

@@ -8,15 +8,19 @@
 // RN_f16(q*s + RN_f16(-z*s)); invalid ids contribute zero, duplicates keep their own
 // weights.
 //
+// The step moves ~7 MB, about 28 KB per CU, so it is bound by memory latency: both kernels
+// issue all of a lane's weight loads at once (compile-time group count per lane) before
+// staging the activations, so weights and activations arrive in one round trip.
 // Kernel 1 (W13 + SwiGLU): one workgroup per (route, 8 consecutive n).  A wave holds
 // four 16-lane row groups: (gate n, up n, gate n+1, up n+1); lane j of a group owns
 // the groups of 32 k  g = j, j+16, ...: one coalesced 16-byte code load per group plus
 // its scale and zero.  x sits in LDS, permuted so that each dword holds the pair
 // (k, k+4) that matches the nibble extraction.  Order: per lane, groups ascending,
 // inside a group 16 dot2 steps ascending; then a butterfly over the 16 lanes.
-// Kernel 2 (W2 + ordered sum): one workgroup per 32 outputs; thread (r, o) computes
-// y_r[o] over its row's 5 groups (lane-per-row, act[r] broadcast from LDS), rounds
-// it to float16 into LDS; then 32 threads sum the routes in order with fmaf.
+// Kernel 2 (W2 + ordered sum): one workgroup per 32 outputs, one wave per route reading the
+// route's 32 rows as contiguous 16-byte group pieces; per (route, output) the group partials
+// are added in group order and rounded to float16; then 32 threads sum the routes in order
+// with fmaf.
 #include "dev_common.h"
 #include "launch.h"
 
@@ -26,21 +30,40 @@ namespace {
 
 constexpr int kGrpStride = 80;  // 32 f16 (64 B) + 16 B padding per group of 32 in LDS
 
-// Copy n16 halves from src into LDS groups of 32 in (k, k+4) pair order.
-__device__ __forceinline__ void stage_pairs(uint8_t* lds, const uint16_t* __restrict__ src, int n16) {
-  const int nblk = n16 >> 3;  // 8-k blocks
-  for (int b = threadIdx.x; b < nblk; b += blockDim.x) {
-    const uint4 v = *reinterpret_cast<const uint4*>(src + 8 * b);
-    const uint16_t e[8] = {(uint16_t)v.x, (uint16_t)(v.x >> 16), (uint16_t)v.y, (uint16_t)(v.y >> 16),
-                           (uint16_t)v.z, (uint16_t)(v.z >> 16), (uint16_t)v.w, (uint16_t)(v.w >> 16)};
-    uint4 o;
-    o.x = (uint32_t)e[0] | ((uint32_t)e[4] << 16);
-    o.y = (uint32_t)e[1] | ((uint32_t)e[5] << 16);
-    o.z = (uint32_t)e[2] | ((uint32_t)e[6] << 16);
-    o.w = (uint32_t)e[3] | ((uint32_t)e[7] << 16);
-    const int g = b >> 2;
-    *reinterpret_cast<uint4*>(lds + g * kGrpStride + (b & 3) * 16) = o;
+// Copy rows of n16 halves (nrows contiguous rows starting at src) into LDS groups of 32 in (k, k+4)
+// pair order, row r at lds + r * row_bytes.  The work is flattened over all rows, and each thread issues
+// up to kStageAhead of its 16-byte loads before writing any of them (one memory round trip instead of
+// one per row or per loop pass); any remainder goes through a plain loop.
+constexpr int kStageAhead = 4;
+
+__device__ __forceinline__ void stage_block(uint8_t* lds, int row_bytes, int bpr, int b, uint4 v) {
+  const int rr = b / bpr, blk = b - rr * bpr;
+  uint4 o;
+  o.x = (v.x & 0xffffu) | (v.z << 16);
+  o.y = (v.x >> 16) | (v.z & 0xffff0000u);
+  o.z = (v.y & 0xffffu) | (v.w << 16);
+  o.w = (v.y >> 16) | (v.w & 0xffff0000u);
+  *reinterpret_cast<uint4*>(lds + rr * row_bytes + (blk >> 2) * kGrpStride + (blk & 3) * 16) = o;
+}
+
+__device__ __forceinline__ void stage_pairs(uint8_t* lds, const uint16_t* __restrict__ src, int n16, int nrows,
+                                            int row_bytes) {
+  const int bpr = n16 >> 3;  // 8-k blocks per row
+  const int nb = nrows * bpr;
+  const uint4* s4 = reinterpret_cast<const uint4*>(src);
+  uint4 v[kStageAhead];
+#pragma unroll
+  for (int j = 0; j < kStageAhead; ++j) {
+    const int b = threadIdx.x + j * (int)blockDim.x;
+    if (b < nb) v[j] = s4[b];
   }
+#pragma unroll
+  for (int j = 0; j < kStageAhead; ++j) {
+    const int b = threadIdx.x + j * (int)blockDim.x;
+    if (b < nb) stage_block(lds, row_bytes, bpr, b, v[j]);
+  }
+  for (int b = threadIdx.x + kStageAhead * (int)blockDim.x; b < nb; b += blockDim.x)
+    stage_block(lds, row_bytes, bpr, b, s4[b]);
 }
 
 // Dot product of one group of 32 codes (16 bytes) with 32 LDS activations.
@@ -66,7 +89,9 @@ __device__ __forceinline__ _Float16 group_bias(const uint8_t* expert, const AwqL
   else return f16_from_bits(reinterpret_cast<const uint16_t*>(expert + L.meta2_off)[idx]);
 }
 
-template <int ML>
+// GPL: groups per lane (compile-time, so every weight load of a lane is issued at once before the
+// activations are staged); 0 = runtime loop for shapes outside the unrolled range.
+template <int ML, int GPL>
 __global__ void __launch_bounds__(256) awq_w13_kernel(int E, int H, int I, const uint16_t* __restrict__ x,
                                                       const int32_t* __restrict__ ids,
                                                       const uint8_t* __restrict__ bank, AwqLayout L,
@@ -80,8 +105,6 @@ __global__ void __launch_bounds__(256) awq_w13_kernel(int E, int H, int I, const
     if (tid < 8 && nb + tid < I) act[(size_t)r * I + nb + tid] = 0;
     return;
   }
-  stage_pairs(lds, x, H);
-  __syncthreads();
   const int lane = tid & 63;
   const int j = lane & 15;
   const int rg = lane >> 4;
@@ -92,13 +115,41 @@ __global__ void __launch_bounds__(256) awq_w13_kernel(int E, int H, int I, const
   const uint8_t* codes = expert + (size_t)row * (H >> 1);
   const uint16_t* scales = reinterpret_cast<const uint16_t*>(expert + L.scale_off);
   float acc = 0.f;
-  if (n < I) {
-    for (int g = j; g < G; g += 16) {
-      const u32x4 c = *reinterpret_cast<const u32x4*>(codes + 16 * g);
-      const int64_t mi = (int64_t)row * G + g;
-      const _Float16 s = f16_from_bits(scales[mi]);
-      const _Float16 b = group_bias<ML>(expert, L, mi, s);
-      acc = awq_group_dot(c, s, b, lds + g * kGrpStride, acc);
+  if constexpr (GPL > 0) {
+    u32x4 c[GPL];
+    _Float16 sv[GPL], bv[GPL];
+    if (n < I) {
+#pragma unroll
+      for (int i = 0; i < GPL; ++i) {
+        const int g = j + 16 * i;
+        if (g < G) {
+          const int64_t mi = (int64_t)row * G + g;
+          c[i] = *reinterpret_cast<const u32x4*>(codes + 16 * g);
+          sv[i] = f16_from_bits(scales[mi]);
+          bv[i] = group_bias<ML>(expert, L, mi, sv[i]);
+        }
+      }
+    }
+    stage_pairs(lds, x, H, 1, 0);
+    __syncthreads();
+    if (n < I) {
+#pragma unroll
+      for (int i = 0; i < GPL; ++i) {
+        const int g = j + 16 * i;
+        if (g < G) acc = awq_group_dot(c[i], sv[i], bv[i], lds + g * kGrpStride, acc);
+      }
+    }
+  } else {
+    stage_pairs(lds, x, H, 1, 0);
+    __syncthreads();
+    if (n < I) {
+      for (int g = j; g < G; g += 16) {
+        const u32x4 c = *reinterpret_cast<const u32x4*>(codes + 16 * g);
+        const int64_t mi = (int64_t)row * G + g;
+        const _Float16 s = f16_from_bits(scales[mi]);
+        const _Float16 b = group_bias<ML>(expert, L, mi, s);
+        acc = awq_group_dot(c, s, b, lds + g * kGrpStride, acc);
+      }
     }
   }
   acc = group_sum<16>(acc);
@@ -111,8 +162,84 @@ __global__ void __launch_bounds__(256) awq_w13_kernel(int E, int H, int I, const
   }
 }
 
+// Kernel 2 (W2 + ordered sum): one workgroup per kW2Rows outputs, one wave per route.  Wave r reads the
+// route's kW2Rows consecutive rows (kW2Rows * I/2 contiguous code bytes) as 16-byte pieces
+// p = lane + 64 j: piece p is group p % G of row p / G, and since the metadata planes are row-major its
+// scale and zero are element p of the block's metadata run, so every load is coalesced.  The group
+// partials go through LDS; per (route, row) they are added in group order, rounded to float16, and
+// kW2Rows threads add the routes in order.  PPL = pieces per lane (compile-time: all loads at once).
+constexpr int kW2Rows = 32;
+
+template <int ML, int PPL>
+__global__ void __launch_bounds__(1024) awq_w2_kernel(int E, int topk, int H, int I,
+                                                      const int32_t* __restrict__ ids,
+                                                      const float* __restrict__ router_w,
+                                                      const uint8_t* __restrict__ bank, AwqLayout L,
+                                                      const uint16_t* __restrict__ act, uint16_t* __restrict__ out) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int G = I >> 5;
+  const int act_bytes = G * kGrpStride;  // per route
+  float* part = reinterpret_cast<float*>(lds + topk * act_bytes);  // [topk][kW2Rows][G]
+  float* ys = part + topk * kW2Rows * G;                           // [topk][kW2Rows]
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int r = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int o0 = blockIdx.x * kW2Rows;
+  const int nrows = min(kW2Rows, H - o0);
+  const int np = nrows * G;
+  const int e = ids[r];
+  const bool live = e >= 0 && e < E;
+  const uint8_t* expert = bank + (size_t)(live ? e : 0) * L.expert_bytes;
+  const uint8_t* codes = expert + (size_t)o0 * (I >> 1);
+  const uint16_t* scales = reinterpret_cast<const uint16_t*>(expert + L.scale_off);
+  const int64_t m0 = (int64_t)o0 * G;
+  u32x4 c[PPL];
+  _Float16 sv[PPL], bv[PPL];
+  if (live) {
+#pragma unroll
+    for (int j = 0; j < PPL; ++j) {
+      const int pc = lane + 64 * j;
+      if (pc < np) {
+        c[j] = *reinterpret_cast<const u32x4*>(codes + 16 * pc);
+        sv[j] = f16_from_bits(scales[m0 + pc]);
+        bv[j] = group_bias<ML>(expert, L, m0 + pc, sv[j]);
+      }
+    }
+  }
+  stage_pairs(lds, act, I, topk, act_bytes);
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < PPL; ++j) {
+    const int pc = lane + 64 * j;
+    if (pc < np) {
+      const int g = pc % G;
+      part[(r * kW2Rows) * G + pc] =
+          live ? awq_group_dot(c[j], sv[j], bv[j], lds + r * act_bytes + g * kGrpStride, 0.f) : 0.f;
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < topk * nrows; i += blockDim.x) {
+    const int rr = i / nrows, row = i - rr * nrows;
+    const float* pp = part + (rr * kW2Rows + row) * G;
+    float y = 0.f;
+    for (int g = 0; g < G; ++g) y += pp[g];
+    ys[rr * kW2Rows + row] = (float)(_Float16)y;  // per-route float16 materialisation
+  }
+  __syncthreads();
+  if (tid < nrows) {
+    float sum = 0.f;
+    for (int rr = 0; rr < topk; ++rr) {
+      const int er = ids[rr];
+      if (er >= 0 && er < E) sum = fmaf(router_w[rr], ys[rr * kW2Rows + tid], sum);
+    }
+    out[o0 + tid] = __builtin_bit_cast(uint16_t, (_Float16)sum);
+  }
+}
+
+// General W2 form (any I the entry point accepts): thread (r, o) computes y_r[o] over its row's groups
+// with act[r] broadcast from LDS, rounds it to float16; then 32 threads sum the routes in order.
 template <int ML>
-__global__ void __launch_bounds__(512) awq_w2_kernel(int E, int topk, int H, int I,
+__global__ void __launch_bounds__(512) awq_w2_rows_kernel(int E, int topk, int H, int I,
                                                      const int32_t* __restrict__ ids,
                                                      const float* __restrict__ router_w,
                                                      const uint8_t* __restrict__ bank, AwqLayout L,
@@ -122,7 +249,7 @@ __global__ void __launch_bounds__(512) awq_w2_kernel(int E, int topk, int H, int
   const int act_bytes = G * kGrpStride;  // per route
   float* ys = reinterpret_cast<float*>(lds + topk * act_bytes);  // [topk][32]
   const int tid = threadIdx.x;
-  for (int r = 0; r < topk; ++r) stage_pairs(lds + r * act_bytes, act + (size_t)r * I, I);
+  stage_pairs(lds, act, I, topk, act_bytes);
   __syncthreads();
   const int r = tid >> 5;
   const int ol = tid & 31;
@@ -166,21 +293,66 @@ hipError_t launch_moe_awq_m1(int E, int topk, int H, int I, const uint16_t* x, c
   const AwqLayout L2 = awq_layout(H, I, meta_layout);
   const size_t lds13 = (size_t)(H / 32) * kGrpStride;
   const dim3 g13(topk, (I + 7) / 8);
-  if (meta_layout == 3)
-    hipLaunchKernelGGL(awq_w13_kernel<3>, g13, dim3(256), lds13, st, E, H, I, x, ids, w13, L13, act);
-  else
-    hipLaunchKernelGGL(awq_w13_kernel<4>, g13, dim3(256), lds13, st, E, H, I, x, ids, w13, L13, act);
+  const int gpl13 = (H / 32 + 15) / 16;  // groups per lane in W13
+#define WQ_W13(ML, P)                                                                                     \
+  hipLaunchKernelGGL((awq_w13_kernel<ML, P>), g13, dim3(256), lds13, st, E, H, I, x, ids, w13, L13, act)
+#define WQ_W13_ML(ML)                                                                     \
+  switch (gpl13) {                                                                        \
+    case 1: WQ_W13(ML, 1); break;                                                         \
+    case 2: WQ_W13(ML, 2); break;                                                         \
+    case 3: WQ_W13(ML, 3); break;                                                         \
+    case 4: WQ_W13(ML, 4); break;                                                         \
+    case 5: WQ_W13(ML, 5); break;                                                         \
+    case 6: WQ_W13(ML, 6); break;                                                         \
+    case 7: WQ_W13(ML, 7); break;                                                         \
+    case 8: WQ_W13(ML, 8); break;                                                         \
+    default: WQ_W13(ML, 0); break;                                                        \
+  }
+  if (meta_layout == 3) {
+    WQ_W13_ML(3)
+  } else {
+    WQ_W13_ML(4)
+  }
+#undef WQ_W13_ML
+#undef WQ_W13
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const size_t lds2 = (size_t)topk * (I / 32) * kGrpStride + (size_t)topk * 32 * 4;
-  const int threads = (topk * 32 + 63) / 64 * 64;
-  const dim3 g2((H + 31) / 32);
-  if (meta_layout == 3)
-    hipLaunchKernelGGL(awq_w2_kernel<3>, g2, dim3(threads), lds2, st, E, topk, H, I, ids, router_w, w2, L2, act,
-                       out);
-  else
-    hipLaunchKernelGGL(awq_w2_kernel<4>, g2, dim3(threads), lds2, st, E, topk, H, I, ids, router_w, w2, L2, act,
-                       out);
+  const size_t lds2 = (size_t)topk * (I / 32) * kGrpStride + (size_t)topk * kW2Rows * (I / 32 + 1) * 4;
+  const int ppl2 = (kW2Rows * (I / 32) + 63) / 64;  // 16-byte pieces per lane in W2
+  if (ppl2 <= 8 && lds2 <= 65536) {
+    const dim3 g2((H + kW2Rows - 1) / kW2Rows);
+#define WQ_W2(ML, P)                                                                                          \
+  hipLaunchKernelGGL((awq_w2_kernel<ML, P>), g2, dim3(64 * topk), lds2, st, E, topk, H, I, ids, router_w, w2, L2, \
+                     act, out)
+#define WQ_W2_ML(ML)            \
+  switch (ppl2) {               \
+    case 1: WQ_W2(ML, 1); break; \
+    case 2: WQ_W2(ML, 2); break; \
+    case 3: WQ_W2(ML, 3); break; \
+    case 4: WQ_W2(ML, 4); break; \
+    case 5: WQ_W2(ML, 5); break; \
+    case 6: WQ_W2(ML, 6); break; \
+    case 7: WQ_W2(ML, 7); break; \
+    default: WQ_W2(ML, 8); break; \
+  }
+    if (meta_layout == 3) {
+      WQ_W2_ML(3)
+    } else {
+      WQ_W2_ML(4)
+    }
+#undef WQ_W2_ML
+#undef WQ_W2
+  } else {
+    const size_t ldsr = (size_t)topk * (I / 32) * kGrpStride + (size_t)topk * 32 * 4;
+    const int threads = (topk * 32 + 63) / 64 * 64;
+    const dim3 g2((H + 31) / 32);
+    if (meta_layout == 3)
+      hipLaunchKernelGGL(awq_w2_rows_kernel<3>, g2, dim3(threads), ldsr, st, E, topk, H, I, ids, router_w, w2, L2,
+                         act, out);
+    else
+      hipLaunchKernelGGL(awq_w2_rows_kernel<4>, g2, dim3(threads), ldsr, st, E, topk, H, I, ids, router_w, w2, L2,
+                         act, out);
+  }
   return hipGetLastError();
 }
 
