@@ -52,6 +52,8 @@ def parse():
                     help="only run a plain 1 GiB device copy (counter calibration for rocprofv3 --pmc)")
     ap.add_argument("--counters", type=int, default=0,
                     help="only run this many plain (non-graph) headline steps, for rocprofv3 --pmc passes")
+    ap.add_argument("--prefill-counters", type=int, default=0,
+                    help="only run this many plain NVFP4 M=512 prefill steps, for rocprofv3 --pmc passes")
     ap.add_argument("--json-out", default=None)
     return ap.parse_args()
 
@@ -158,10 +160,13 @@ def fp8_decode(torch, wq, synth, K, W, copies=4):
                 dn_alg=dn_alg, copies=copies, data=d)
 
 
-def nvfp4_weights(torch, synth, oracle, dev):
+def nvfp4_weights(torch, wq, synth, dev):
+    """Config-3 weights packed into Block64 records by the library's own packer on the device."""
     w = synth.nvfp4_mlp_weights()
-    blk = {n: torch.from_numpy(oracle.block64_pack(w["wp_" + n], w["ws_" + n])).to(dev) for n in ("gate", "up", "down")}
+    blk = {n: wq.nvfp4_pack_block64(torch.from_numpy(w["wp_" + n]).to(dev), torch.from_numpy(w["ws_" + n]).to(dev))
+           for n in ("gate", "up", "down")}
     gs = {n: float(w["gs_" + n]) for n in ("gate", "up", "down")}
+    torch.cuda.synchronize()
     return blk, gs
 
 
@@ -187,12 +192,16 @@ def nvfp4_run(torch, wq, synth, blk, gs, M, K, copies, outlier):
     return dict(t=t, K=K, M=M, gu_ms=gu_ms, dn_ms=dn_ms, copies=copies)
 
 
-def awq_run(torch, wq, synth, oracle, K):
+def awq_run(torch, wq, synth, K):
     dev = torch.device("cuda:0")
     d = synth.awq_moe()
     E, topk, HH, II = 512, 10, 2560, 160
-    b13 = torch.from_numpy(oracle.awq_pack_bank(*d["w13"], 3)).to(dev)
-    b2 = torch.from_numpy(oracle.awq_pack_bank(*d["w2"], 3)).to(dev)
+    def bank(codes, scales, zeros):   # the library's packer, on the device
+        return wq.awq_pack_bank(torch.from_numpy(codes).to(dev), torch.from_numpy(scales.view("int16")).to(dev),
+                                torch.from_numpy(zeros).to(dev), 3)
+    b13 = bank(*d["w13"])
+    b2 = bank(*d["w2"])
+    torch.cuda.synchronize()
     x = torch.from_numpy(d["x_bits"].view("int16")).to(dev).view(torch.float16)
     rw = torch.from_numpy(d["router_w"]).to(dev)
     hot = torch.from_numpy(d["ids"]).to(dev)
@@ -243,14 +252,14 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (each MI355X runs the "
-              "kernels on its own shard; see DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU; runs over several GPUs are not supported (each MI355X would run "
+              "the same kernels on its own shard of the intermediate dimension). Run with --gpus 1.",
+              file=sys.stderr)
         sys.exit(2)
 
     import numpy as np  # noqa: F401
     import torch
 
-    import oracle
     import synth
     import weight_quantized_mlp_amd as wq
 
@@ -283,6 +292,20 @@ def main():
         log(f"counter steps done: {args.counters}")
         return
 
+    if args.prefill_counters:
+        blk, gs = nvfp4_weights(torch, wq, synth, dev)
+        M = 512
+        xb, _ = synth.nvfp4_x(M, outlier_frac=0.01)
+        x = torch.from_numpy(xb.view("int16")).to(dev).view(torch.bfloat16)
+        out = torch.empty((M, H), dtype=torch.float32, device=dev)
+        ws = torch.empty(wq.mlp_workspace_bytes(wq.WQ_FMT_NVFP4, M, H, I), dtype=torch.uint8, device=dev)
+        for _ in range(args.prefill_counters):
+            wq.mlp_nvfp4_run(x, blk["gate"], gs["gate"], blk["up"], gs["up"], blk["down"], gs["down"], out=out,
+                             workspace=ws)
+        torch.cuda.synchronize()
+        log(f"prefill counter steps done: {args.prefill_counters}")
+        return
+
     K, W = args.steps, args.warmup
     log(f"fp8 decode: K={K} W={W}")
     r = fp8_decode(torch, wq, synth, K, W)
@@ -300,7 +323,7 @@ def main():
         {"nvfp4_decode", "nvfp4_prefill_512", "nvfp4_prefill_8192", "awq"} if args.extras == "all"
         else set(args.extras.split(",")))
     if want & {"nvfp4_decode", "nvfp4_prefill_512", "nvfp4_prefill_8192"}:
-        blk, gs = nvfp4_weights(torch, synth, oracle, dev)
+        blk, gs = nvfp4_weights(torch, wq, synth, dev)
         nv_bytes = 3 * (H * I // 64 * 36)
         if "nvfp4_decode" in want:
             n = nvfp4_run(torch, wq, synth, blk, gs, 1, K, 8, 0.0)
@@ -324,7 +347,7 @@ def main():
             log(key, extras[key])
         del blk
     if "awq" in want:
-        a = awq_run(torch, wq, synth, oracle, 480)
+        a = awq_run(torch, wq, synth, 480)
         extras["awq_moe_m1"] = dict(
             hot_us_per_step=round(a["hot_s"] * 1e6, 3), rotating_us_per_step=round(a["rot_s"] * 1e6, 3),
             rotating_GBps=round(a["step_bytes"] / a["rot_s"] / 1e9, 1),
@@ -334,6 +357,7 @@ def main():
 
     torch.cuda.synchronize()
     log(f"cpu baseline (oracle, ~{args.cpu_seconds:.0f} s)")
+    import oracle   # the CPU baseline leg is the only part of the benchmark that uses the oracle
     cpu = cpu_baseline(oracle, r["data"], args.cpu_seconds)
     log("cpu", cpu)
 
