@@ -37,7 +37,7 @@ def one_hot_rows(M, K, ks):
 
 @pytest.mark.parametrize("path,M", [("gemv", 1), ("gemv", 4), ("mfma", 128)])
 @pytest.mark.parametrize("xdt", [torch.float32, torch.bfloat16])
-@pytest.mark.parametrize("K", [256, 5120])
+@pytest.mark.parametrize("K", [256, 320, 5120])
 def test_fp8_one_hot(path, M, xdt, K):
     N = 192
     w, s = fp8_weights(N, K, 5)
@@ -53,7 +53,7 @@ def test_fp8_one_hot(path, M, xdt, K):
 
 @pytest.mark.parametrize("path,M", [("gemv", 1), ("gemv", 4), ("mfma", 128)])
 @pytest.mark.parametrize("xdt", [torch.float32, torch.bfloat16])
-@pytest.mark.parametrize("K", [256, 5120])
+@pytest.mark.parametrize("K", [256, 320, 5120])
 def test_nvfp4_one_hot(path, M, xdt, K):
     N = 192
     wp, ws, gs = synth.nvfp4_tensor(N, K, 3, 21)

@@ -18,12 +18,24 @@
 //     float32, rounded once to float16 for the down GEMM (|act| < 65504 required);
 //   * down: acc * (1/global_scale or channel scale), stored as float32.
 //
-// Tiling: a workgroup of 4 waves computes a (32*MB) x 128 output tile (of both gate
-// and up for the fused kernel).  All waves share the activation tile, staged in LDS
-// (rows padded to 144 bytes: conflict-free 16-byte fragment reads); each wave owns
-// 32 output columns and decodes its own weight fragments straight from global memory
-// into registers, so every decoded fragment feeds MB (x2 with gate+up) MFMAs.  K is
-// walked in steps of 64 (one Block64 record) with the next step's loads in flight.
+// Tiling (both kernels): a workgroup of 4 waves computes a (32*MB) x 128 output tile (of both gate and
+// up for the fused projection).  All waves share the activation tile, staged in LDS; each wave owns 32
+// output columns and decodes its own weight fragments into registers, so every decoded fragment feeds
+// MB (x2 with gate+up) MFMAs.  K is walked in steps of 64 (one Block64 record per column).
+//
+// FP8 weights (mfma_gemm_kernel): activation rows padded to 144 bytes in LDS; weight bytes loaded
+// straight from global memory into registers one K step ahead.
+//
+// NVFP4 weights (nv_gemm_kernel): a lane-per-column load of 36-byte records touches one cache line per
+// lane, and that access pattern, not bandwidth, limited the register-load form.  Here both operands move
+// by direct global->LDS copies (global_load_lds_dwordx4) in a coalesced order: the activation tile
+// (128-byte rows, 16-byte chunk c of row r stored at chunk c ^ (r & 7), so fragment reads are
+// bank-conflict free) in a 2-stage ring, and the weights in blocks of 4 records per column (144
+// contiguous bytes = 9 chunks, 16-byte aligned in the row), one block buffer per wave.  At the start of
+// a block each wave reads the whole block of its columns into registers and immediately refills the
+// buffer with the next block, so the weight copy has four K steps to land.  Inside a K step the
+// activation fragments of sub-step s+1 are read while the MFMAs of sub-step s run; the single barrier
+// per K step sits after the third sub-step.  Two workgroups share a CU (72 KB of LDS each).
 //
 // MFMA v_mfma_f32_32x32x16_f16 operand layout (checked on gfx950): A lane l holds row
 // l%32, k = 8*(l/32) + j; B lane l holds column l%32, same k; D register r of lane l
@@ -31,6 +43,9 @@
 // (0..3) feeds the instruction k' = 8*(l/32) + j with the logical k = 32*(l/32) +
 // 8*s + j, for both operands, so each lane's weight bytes for a whole record are one
 // contiguous 16-byte (NVFP4) or 32-byte (FP8) load.
+#include <atomic>
+#include <type_traits>
+
 #include "dev_common.h"
 #include "launch.h"
 
@@ -265,6 +280,269 @@ __global__ void __launch_bounds__(256, 2) mfma_gemm_kernel(int M, int K, int N, 
   }
 }
 
+// ---- NVFP4: operands by global->LDS copy --------------------------------------------------------
+// Copy 16 bytes per lane from sbase + voff into LDS at lds_base + 16 * lane (lds_base wave-uniform).
+// M0 carries the LDS address; nothing else in these kernels uses M0, so clobbering it is safe (the
+// compiler warns about clobbering a reserved register in general).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_copy16(uint32_t voff, const void* sbase, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds_base)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+// s_waitcnt vmcnt(N) with the other counters left alone (the copies above are invisible to the compiler's
+// own counter tracking, so every wait on them is explicit).
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }   // lgkmcnt(0)
+
+constexpr int kNvMB = 4;                       // 128-row tiles
+constexpr int kNvAStage = 32 * kNvMB * 128;    // bytes per activation stage
+constexpr int nv_wave_wbytes(bool gu) { return (gu ? 2 : 1) * 5 * 1024; }
+constexpr int nv_lds_bytes(bool gu) { return 2 * kNvAStage + 4 * nv_wave_wbytes(gu); }
+
+template <bool GU>
+__global__ void __launch_bounds__(256, 2) nv_gemm_kernel(int M, int K, int N, int ntm, int ntn,
+                                                        const uint16_t* __restrict__ a16,
+                                                        const float* __restrict__ rowscale,
+                                                        const uint8_t* __restrict__ w0, float inv0,
+                                                        const uint8_t* __restrict__ w1, float inv1,
+                                                        void* __restrict__ out) {
+  constexpr int NM = GU ? 2 : 1;
+  constexpr int MB = kNvMB;
+  constexpr int NW = NM * 5;                   // weight copies per wave per block: 288 chunks (+32 pad) per matrix
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int per = gridDim.x >> 3;
+  const int tile = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
+  if (tile >= ntm * ntn) return;
+  const int tm = tile / ntn;
+  const int tn = tile - tm * ntn;
+  const int m0 = tm * 32 * MB;
+  const int n0 = tn * 128;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int li = lane & 31;
+  const int h = lane >> 5;
+  const int nk = K >> 6;
+  const int nblk = (nk + 3) >> 2;
+  const uint32_t rb = (uint32_t)nk * 36u;      // bytes per weight row
+  const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
+  const uint32_t wlds = lds0 + 2 * kNvAStage + wave * nv_wave_wbytes(GU);
+  const uint8_t* wbuf = lds + 2 * kNvAStage + wave * nv_wave_wbytes(GU);
+
+  // Activation chunk p = tid + 256 i: tile row p >> 3, LDS chunk p & 7, global chunk (p & 7) ^ (row & 7).
+  uint32_t aoff[MB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i) {
+    const int p = tid + 256 * i, row = p >> 3, c = p & 7;
+    aoff[i] = (uint32_t)min(m0 + row, M - 1) * (uint32_t)K * 2u + (uint32_t)((c ^ (row & 7)) * 16);
+  }
+  // Weight copy j = 5 t + i of matrix t, slot s = 64 i + lane (slots 288..319 re-read chunks of slots
+  // 0..31): column c = s / 9 of this wave, chunk q = s % 9 of the column's 144-byte block.  The block of
+  // column c of matrix t sits at LDS wbuf + 5120 t + 144 c.
+  uint32_t woff[NW];
+#pragma unroll
+  for (int j = 0; j < NW; ++j) {
+    int s = 64 * (j % 5) + lane;
+    if (s >= 288) s -= 288;
+    const int c = s / 9, q = s - 9 * c;
+    woff[j] = (uint32_t)min(n0 + 32 * wave + c, N - 1) * rb + 16u * (uint32_t)q;
+  }
+  auto copy_a = [&](int kt, int stage) {
+    kt = min(kt, nk - 1);
+    const uint8_t* base = reinterpret_cast<const uint8_t*>(a16) + (size_t)kt * 128;
+    const uint32_t sb = lds0 + stage * kNvAStage;
+#pragma unroll
+    for (int i = 0; i < MB; ++i) lds_copy16(aoff[i], base, __builtin_amdgcn_readfirstlane(sb + (256 * i + 64 * wave) * 16));
+  };
+  // A row whose record count r = nk % 4 is not 0 ends in a short block: it is copied as the last 144
+  // bytes of the row (records 4 - r .. 3 of the window are the valid ones; K >= 256, so the window starts
+  // inside the row) and read_block moves those records down to positions 0 .. r-1.
+  const int rtail = nk & 3;
+  auto copy_w = [&](int blk) {
+    blk = min(blk, nblk - 1);
+    const uint32_t boff = (rtail && blk == nblk - 1) ? rb - 144u : (uint32_t)blk * 144u;
+#pragma unroll
+    for (int j = 0; j < NW; ++j)
+      lds_copy16(woff[j] + boff, j < 5 ? w0 : w1, __builtin_amdgcn_readfirstlane(wlds + 1024 * j));
+  };
+  f32x16 acc[NM][MB];
+#pragma unroll
+  for (int t = 0; t < NM; ++t)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[t][mb][r] = 0.f;
+
+  // Registers of one 4-record block for this lane's column of matrix t: record J's scale dword and the
+  // 16 nibble bytes of its half h (bytes 36 J + 4 + 16 h .. + 15 of the block).
+  struct WBlock { uint32_t nib[4][4]; uint32_t d[4]; };
+  auto shift_block = [&](WBlock* wb, auto Sc) {   // record J <- record J + S
+    constexpr int S = decltype(Sc)::value;
+#pragma unroll
+    for (int t = 0; t < NM; ++t)
+#pragma unroll
+      for (int J = 0; J + S < 4; ++J) {
+        wb[t].d[J] = wb[t].d[J + S];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) wb[t].nib[J][e] = wb[t].nib[J + S][e];
+      }
+  };
+  auto read_block = [&](WBlock* wb, int blk) {
+#pragma unroll
+    for (int t = 0; t < NM; ++t) {
+      const uint8_t* bp = wbuf + 5120 * t + 144 * li;
+#pragma unroll
+      for (int J = 0; J < 4; ++J) wb[t].d[J] = *reinterpret_cast<const uint32_t*>(bp + 36 * J);
+      u32x4 P = *reinterpret_cast<const u32x4*>(bp + 16 * h);          // record 0: chunks h, h+1
+      u32x4 Q = *reinterpret_cast<const u32x4*>(bp + 16 * (1 + h));
+      wb[t].nib[0][0] = P.y; wb[t].nib[0][1] = P.z; wb[t].nib[0][2] = P.w; wb[t].nib[0][3] = Q.x;
+      P = *reinterpret_cast<const u32x4*>(bp + 16 * (2 + h));               // record 1: chunks 2+h, 3+h
+      Q = *reinterpret_cast<const u32x4*>(bp + 16 * (3 + h));
+      wb[t].nib[1][0] = P.z; wb[t].nib[1][1] = P.w; wb[t].nib[1][2] = Q.x; wb[t].nib[1][3] = Q.y;
+      P = *reinterpret_cast<const u32x4*>(bp + 16 * (4 + h));               // record 2: chunks 4+h, 5+h
+      Q = *reinterpret_cast<const u32x4*>(bp + 16 * (5 + h));
+      wb[t].nib[2][0] = P.w; wb[t].nib[2][1] = Q.x; wb[t].nib[2][2] = Q.y; wb[t].nib[2][3] = Q.z;
+      P = *reinterpret_cast<const u32x4*>(bp + 16 * (7 + h));               // record 3: chunk 7+h
+      wb[t].nib[3][0] = P.x; wb[t].nib[3][1] = P.y; wb[t].nib[3][2] = P.z; wb[t].nib[3][3] = P.w;
+    }
+    if (rtail && blk == nblk - 1) {
+      if (rtail == 1) shift_block(wb, std::integral_constant<int, 3>{});
+      else if (rtail == 2) shift_block(wb, std::integral_constant<int, 2>{});
+      else shift_block(wb, std::integral_constant<int, 1>{});
+    }
+  };
+  auto read_a = [&](int stage, int s, f16x8* af) {
+    const uint8_t* ast = lds + stage * kNvAStage;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+      af[mb] = *reinterpret_cast<const f16x8*>(ast + (32 * mb + li) * 128 + (((4 * h + s) ^ (li & 7)) * 16));
+  };
+  // decode sub-step s of record J (exact f16: E2M1 x E4M3 group scale) and run its MFMAs
+  auto mfmas = [&](const WBlock* wb, int J, int s, const f16x8* af) {
+    f16x8 bfr[NM];
+#pragma unroll
+    for (int t = 0; t < NM; ++t) {
+      const f16x2 dsc = e4m3x2_f16<false>(wb[t].d[J] >> (16 * h));   // groups 2h, 2h+1
+      const uint32_t w = wb[t].nib[J][s];
+      const _Float16 g = (s < 2) ? dsc.x : dsc.y;
+      const f16x2 gg = {g, g};
+      const f16x2 p0 = e2m1x2_f16<0>(w) * gg, p1 = e2m1x2_f16<1>(w) * gg, p2 = e2m1x2_f16<2>(w) * gg,
+                  p3 = e2m1x2_f16<3>(w) * gg;
+      bfr[t] = f16x8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+    }
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int t = 0; t < NM; ++t)
+        acc[t][mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[mb], bfr[t], acc[t][mb], 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < MB * NM; ++i) {      // one MFMA, one fragment read, two ALU ops at a time
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i < MB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+    }
+  };
+
+  // Prologue: weight block 0, activation steps 0 and 1; wait for block 0 and step 0 (step 1 may fly),
+  // read block 0 into registers and refill the buffer with block 1.
+  copy_w(0);
+  copy_a(0, 0);
+  copy_a(1, 1);
+  wait_vmem<MB>();
+  __syncthreads();
+  WBlock wb[NM];
+  read_block(wb, 0);
+  wait_lds();
+  copy_w(1);
+  f16x8 af0[MB], af1[MB];
+  read_a(0, 0, af0);
+  // K step kt (stage kt & 1, record J of the block in registers).
+  auto step = [&](int kt, auto Jc) {
+    constexpr int J = decltype(Jc)::value;
+    read_a(kt & 1, 1, af1);
+    mfmas(wb, J, 0, af0);
+    __builtin_amdgcn_sched_barrier(0);
+    read_a(kt & 1, 2, af0);
+    mfmas(wb, J, 1, af1);
+    __builtin_amdgcn_sched_barrier(0);
+    read_a(kt & 1, 3, af1);
+    mfmas(wb, J, 2, af0);
+    __builtin_amdgcn_sched_barrier(0);
+    // Step kt+1's activations were copied at the previous barrier; at record 0 the copy of the next
+    // weight block (issued after them) may still be in flight.
+    if constexpr (J == 0) wait_vmem<NW>();
+    else wait_vmem<0>();
+    __syncthreads();
+    copy_a(kt + 2, kt & 1);                  // every wave is done with this stage
+    read_a((kt + 1) & 1, 0, af0);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(wb, J, 3, af1);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (J == 3) {                  // next block: complete since the wait above
+      read_block(wb, (kt >> 2) + 1);
+      wait_lds();
+      copy_w((kt >> 2) + 2);
+    }
+  };
+  for (int kt = 0; kt < nk; kt += 4) {
+    step(kt, std::integral_constant<int, 0>{});
+    if (kt + 1 < nk) step(kt + 1, std::integral_constant<int, 1>{});
+    if (kt + 2 < nk) step(kt + 2, std::integral_constant<int, 2>{});
+    if (kt + 3 < nk) step(kt + 3, std::integral_constant<int, 3>{});
+  }
+  wait_vmem<0>();                            // the trailing (clamped) copies land before the LDS is released
+
+  const int ncol = n0 + 32 * wave + li;
+  if (ncol >= N) return;
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = m0 + 32 * mb + 8 * (r >> 2) + 4 * h + (r & 3);
+      if (m < M) {
+        const float rs = rowscale ? rowscale[m] : 1.0f;
+        if constexpr (GU) {
+          const float g = acc[0][mb][r] * rs * inv0;
+          const float u = acc[1][mb][r] * rs * inv1;
+          const _Float16 a = (_Float16)(silu_f32(g) * u);
+          reinterpret_cast<uint16_t*>(out)[(size_t)m * N + ncol] = __builtin_bit_cast(uint16_t, a);
+        } else {
+          reinterpret_cast<float*>(out)[(size_t)m * N + ncol] = acc[0][mb][r] * rs * inv0;
+        }
+      }
+    }
+  }
+}
+
+template <bool GU>
+hipError_t nv_dispatch(int M, int K, int N, const uint16_t* a16, const float* rowscale, const uint8_t* w0,
+                       float inv0, const uint8_t* w1, float inv1, void* out, hipStream_t st) {
+  // 72 KB (gate+up) / 52 KB of dynamic LDS: raise the per-kernel limit once per device
+  static std::atomic<uint64_t> raised{0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = (uint64_t)1 << (dev & 63);
+  if (!(raised.load() & bit)) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(nv_gemm_kernel<GU>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, nv_lds_bytes(GU));
+    if (e != hipSuccess) return e;
+    raised.fetch_or(bit);
+  }
+  const int ntn = (N + 127) / 128;
+  const int ntm = (M + 32 * kNvMB - 1) / (32 * kNvMB);
+  const int grid = (ntm * ntn + 7) / 8 * 8;
+  hipLaunchKernelGGL((nv_gemm_kernel<GU>), dim3(grid), dim3(256), nv_lds_bytes(GU), st, M, K, N, ntm, ntn, a16,
+                     rowscale, w0, inv0, w1, inv1, out);
+  return hipGetLastError();
+}
+
 template <int FMT, bool GU>
 hipError_t gemm_dispatch(int M, int K, int N, const uint16_t* a16, const float* rowscale, const uint8_t* w0,
                          const float* cs0, float inv0, const uint8_t* w1, const float* cs1, float inv1, void* out,
@@ -301,6 +579,7 @@ hipError_t launch_rowscale_f16(int M, int K, const void* x, XType xt, uint16_t* 
 hipError_t launch_mfma_gateup(int fmt, int M, int K, int N, const uint16_t* x16, const float* rowscale,
                               const uint8_t* w0, const float* cs0, float inv0, const uint8_t* w1,
                               const float* cs1, float inv1, uint16_t* act16, hipStream_t st) {
+  if (fmt == 1 && K >= 256) return nv_dispatch<true>(M, K, N, x16, rowscale, w0, inv0, w1, inv1, act16, st);
   if (fmt == 1)
     return gemm_dispatch<1, true>(M, K, N, x16, rowscale, w0, cs0, inv0, w1, cs1, inv1, act16, st);
   return gemm_dispatch<0, true>(M, K, N, x16, rowscale, w0, cs0, inv0, w1, cs1, inv1, act16, st);
@@ -308,6 +587,7 @@ hipError_t launch_mfma_gateup(int fmt, int M, int K, int N, const uint16_t* x16,
 
 hipError_t launch_mfma_linear(int fmt, int M, int K, int N, const uint16_t* a16, const float* rowscale,
                               const uint8_t* w, const float* cs, float inv, float* y, hipStream_t st) {
+  if (fmt == 1 && K >= 256) return nv_dispatch<false>(M, K, N, a16, rowscale, w, inv, nullptr, 0.f, y, st);
   if (fmt == 1) return gemm_dispatch<1, false>(M, K, N, a16, rowscale, w, cs, inv, nullptr, nullptr, 0.f, y, st);
   return gemm_dispatch<0, false>(M, K, N, a16, rowscale, w, cs, inv, nullptr, nullptr, 0.f, y, st);
 }
