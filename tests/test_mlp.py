@@ -111,6 +111,20 @@ def test_nvfp4_prefill_M512(nv_big):
     gate(y, nv_ref(W, oracle.bf16_bits_to_f64(xb)), what="nvfp4 M=512 (mfma)")
 
 
+def test_nvfp4_prefill_M512_split_k_reproducible(nv_big):
+    # At M=512 the last round of gate/up tiles and every down tile are split along K and finished by
+    # an ordered sum of the parts: two runs give the same bits, and the split rows (the last 128-row
+    # band, whose upper column tiles form the split round of gate/up) match the oracle.
+    blk, gs, W, dblk = nv_big
+    xb, _ = synth.nvfp4_x(512, config_id=7, outlier_frac=0.01)
+    x = bf16_dev(xb)
+    y1 = host(nv_run(dblk, gs, x))
+    y2 = host(nv_run(dblk, gs, x))
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+    band = np.arange(384, 512)
+    gate(y1[band], nv_ref(W, oracle.bf16_bits_to_f64(xb[band])), what="nvfp4 M=512 split band")
+
+
 def test_nvfp4_prefill_M8192_sampled(nv_big):
     blk, gs, W, dblk = nv_big
     xb, rows = synth.nvfp4_x(8192, outlier_frac=0.01)

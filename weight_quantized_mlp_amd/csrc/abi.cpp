@@ -10,6 +10,7 @@
 // as WQ_ELAUNCH; there is no alternative or host path.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -119,11 +120,19 @@ size_t wbytes(int fmt, int64_t N, int64_t K) {
   return fmt == WQ_FMT_FP8W ? (size_t)N * (size_t)K : (size_t)N * (size_t)(K / 64) * 36;
 }
 
+// Split-K scratch of the MFMA path: gate+up and down run one after the other and share it.
+size_t mlp_partials(int fmt, int64_t M, int64_t H, int64_t I) {
+  const int f = fmt == WQ_FMT_NVFP4 ? 1 : 0;
+  return std::max(wq::mfma_partial_bytes(f, (int)M, (int)H, (int)I, true),
+                  wq::mfma_partial_bytes(f, (int)M, (int)I, (int)H, false));
+}
+
 // Workspace of the two-layer MLP; 0 means "invalid".
 size_t mlp_ws(int fmt, int64_t M, int64_t H, int64_t I, int flags) {
   if (M <= 0 || H <= 0 || I <= 0 || M > kMaxDim || H > kMaxDim || I > kMaxDim) return 0;
   if (pick_path(M, flags) == WQ_PATH_GEMV) return align256((size_t)M * I * 4);
-  return align256((size_t)M * H * 2) + align256((size_t)M * 4) + align256((size_t)M * I * 2);
+  return align256((size_t)M * H * 2) + align256((size_t)M * 4) + align256((size_t)M * I * 2) +
+         align256(mlp_partials(fmt, M, H, I));
 }
 
 bool shape_ok(int fmt, int path, int64_t H, int64_t I, int x_dtype) {
@@ -188,15 +197,20 @@ int mlp_run(int fmt, int64_t M, int64_t H, int64_t I, const void* x, int x_dtype
   uint16_t* x16 = reinterpret_cast<uint16_t*>(base);
   float* rs = reinterpret_cast<float*>(base + align256((size_t)M * H * 2));
   uint16_t* act16 = reinterpret_cast<uint16_t*>(base + align256((size_t)M * H * 2) + align256((size_t)M * 4));
+  float* partials = mlp_partials(fmt, M, H, I)
+                        ? reinterpret_cast<float*>(base + align256((size_t)M * H * 2) + align256((size_t)M * 4) +
+                                                   align256((size_t)M * I * 2))
+                        : nullptr;
   const int f = fmt == WQ_FMT_NVFP4 ? 1 : 0;
   if (do_gu) {
     rc = launched(wq::launch_rowscale_f16(m, h, x, xt, x16, rs, st));
     if (rc == WQ_OK)
       rc = launched(wq::launch_mfma_gateup(f, m, h, i, x16, rs, wg, sg, f ? 1.0f / gg : 0.f, wu, su,
-                                           f ? 1.0f / gu : 0.f, act16, st));
+                                           f ? 1.0f / gu : 0.f, act16, partials, st));
   }
   if (rc == WQ_OK && do_down)
-    rc = launched(wq::launch_mfma_linear(f, m, i, h, act16, nullptr, wd, sd, f ? 1.0f / gd : 0.f, out, st));
+    rc = launched(wq::launch_mfma_linear(f, m, i, h, act16, nullptr, wd, sd, f ? 1.0f / gd : 0.f, out, partials,
+                                         st));
   return rc;
 }
 
@@ -335,7 +349,8 @@ size_t qlinear_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K, int fla
   if ((fmt != WQ_FMT_FP8W && fmt != WQ_FMT_NVFP4) || flags < WQ_PATH_AUTO || flags > WQ_PATH_MFMA) return 0;
   if (M <= 0 || N <= 0 || K <= 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return 0;
   if (pick_path(M, flags) == WQ_PATH_GEMV) return 0;
-  return align256((size_t)M * K * 2) + align256((size_t)M * 4);
+  return align256((size_t)M * K * 2) + align256((size_t)M * 4) +
+         align256(wq::mfma_partial_bytes(fmt == WQ_FMT_NVFP4 ? 1 : 0, (int)M, (int)K, (int)N, false));
 }
 
 int qlinear_run(int fmt, int64_t M, int64_t N, int64_t K, const void* x, int x_dtype, const uint8_t* w,
@@ -376,10 +391,13 @@ int qlinear_run(int fmt, int64_t M, int64_t N, int64_t K, const void* x, int x_d
   uint8_t* base = reinterpret_cast<uint8_t*>(workspace);
   uint16_t* x16 = reinterpret_cast<uint16_t*>(base);
   float* rs = reinterpret_cast<float*>(base + align256((size_t)M * K * 2));
+  const int f = fmt == WQ_FMT_NVFP4 ? 1 : 0;
+  float* partials = wq::mfma_partial_bytes(f, (int)M, (int)K, (int)N, false)
+                        ? reinterpret_cast<float*>(base + align256((size_t)M * K * 2) + align256((size_t)M * 4))
+                        : nullptr;
   rc = launched(wq::launch_rowscale_f16((int)M, (int)K, x, xt, x16, rs, st));
   if (rc == WQ_OK)
-    rc = launched(wq::launch_mfma_linear(fmt == WQ_FMT_NVFP4 ? 1 : 0, (int)M, (int)K, (int)N, x16, rs, w, scale, inv,
-                                         y, st));
+    rc = launched(wq::launch_mfma_linear(f, (int)M, (int)K, (int)N, x16, rs, w, scale, inv, y, partials, st));
   return rc;
 }
 

@@ -36,13 +36,17 @@ hipError_t launch_rowscale_f16(int M, int K, const void* x, XType xt, uint16_t* 
                                hipStream_t st);
 // fmt 0 FP8 (w = [N,K] codes, colscale[n]) / 1 NVFP4 (w = Block64, uniform inv).
 // gate+up: act16[m,n] = f16(silu(g) * u) with g = rowscale[m]*colscale(n)*acc.
+// partials: float32 scratch of mfma_partial_bytes(fmt, M, K, N, gu) bytes (NULL allowed when that is 0);
+// the NVFP4 GEMM splits the tiles of an underfilled last round along K and finishes them from there.
+size_t mfma_partial_bytes(int fmt, int M, int K, int N, bool gu);
 hipError_t launch_mfma_gateup(int fmt, int M, int K, int N, const uint16_t* x16, const float* rowscale,
                               const uint8_t* w0, const float* cs0, float inv0,
                               const uint8_t* w1, const float* cs1, float inv1,
-                              uint16_t* act16, hipStream_t st);
+                              uint16_t* act16, float* partials, hipStream_t st);
 // single matrix: y[m,n] = rowscale[m] (1 if null) * colscale(n) * sum_k a16[m,k] dq(w[n,k]).
 hipError_t launch_mfma_linear(int fmt, int M, int K, int N, const uint16_t* a16, const float* rowscale,
-                              const uint8_t* w, const float* cs, float inv, float* y, hipStream_t st);
+                              const uint8_t* w, const float* cs, float inv, float* y, float* partials,
+                              hipStream_t st);
 
 // ---- AWQ routed-expert single-token step ------------------------------------------------------
 hipError_t launch_moe_awq_m1(int E, int topk, int H, int I, const uint16_t* x, const int32_t* ids,

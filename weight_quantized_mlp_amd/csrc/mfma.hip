@@ -43,6 +43,7 @@
 // (0..3) feeds the instruction k' = 8*(l/32) + j with the logical k = 32*(l/32) +
 // 8*s + j, for both operands, so each lane's weight bytes for a whole record are one
 // contiguous 16-byte (NVFP4) or 32-byte (FP8) load.
+#include <algorithm>
 #include <atomic>
 #include <type_traits>
 
@@ -305,20 +306,91 @@ constexpr int kNvAStage = 32 * kNvMB * 128;    // bytes per activation stage
 constexpr int nv_wave_wbytes(bool gu) { return (gu ? 2 : 1) * 5 * 1024; }
 constexpr int nv_lds_bytes(bool gu) { return 2 * kNvAStage + 4 * nv_wave_wbytes(gu); }
 
+// Work plan of one launch, a pure function of the shape.  128x128 tiles; with two workgroups on each
+// of the 256 CUs there are 512 slots.  When the last round of tiles would leave most slots idle (or
+// there are fewer tiles than slots at all) the tiles of that round are split along K into S parts of
+// whole 4-record weight blocks: the parts run first, store raw float32 partial tiles, and a second
+// kernel adds the S parts of every element in part order and applies the epilogue.  The sum order
+// is fixed by the shape, so results are reproducible.
+constexpr int kNvSlots = 512;
+constexpr size_t kNvMaxPartials = (size_t)64 << 20;
+struct NvPlan {
+  int ntm, ntn, tiles;   // tile grid
+  int full;              // tiles [0, full) run whole
+  int S, bps;            // split tiles [full, tiles) run as S parts of bps blocks (S = 1: none)
+  int units, units_grid; // (tiles - full) * S parts; rounded up to a multiple of 8
+};
+inline NvPlan nv_plan(int M, int K, int N, bool gu) {
+  NvPlan p{};
+  p.ntm = (M + 127) / 128;
+  p.ntn = (N + 127) / 128;
+  p.tiles = p.ntm * p.ntn;
+  const int nblk = (K / 64 + 3) / 4;
+  int tail = 0;
+  if (M >= 128) {
+    if (p.tiles < kNvSlots) {
+      tail = p.tiles;
+    } else {
+      const int rounds = (p.tiles + kNvSlots - 1) / kNvSlots;
+      tail = p.tiles - (rounds - 1) * kNvSlots;
+      if (tail * 10 >= kNvSlots * 9) tail = 0;   // a nearly full last round runs whole
+    }
+  }
+  // S minimises the rounds of parts per tile, ceil(tail * S / slots) / S (ties: fewer parts)
+  int S = 1;
+  if (tail > 0) {
+    const size_t per_part = (size_t)(gu ? 2 : 1) * 128 * 128 * 4;
+    double best = 1.0;
+    for (int s = 2; s <= std::min(8, nblk); ++s) {
+      if ((size_t)tail * s * per_part > kNvMaxPartials) break;
+      const double t = (double)((tail * s + kNvSlots - 1) / kNvSlots) / s;
+      if (t < best - 1e-9) { best = t; S = s; }
+    }
+  }
+  if (S < 2) { tail = 0; S = 1; }
+  p.bps = (nblk + S - 1) / S;
+  p.S = S > 1 ? (nblk + p.bps - 1) / p.bps : 1;   // no empty parts
+  p.full = p.tiles - tail;
+  p.units = tail * p.S;
+  p.units_grid = (p.units + 7) / 8 * 8;
+  return p;
+}
+inline size_t nv_partial_bytes(const NvPlan& p, bool gu) {
+  return (size_t)p.units * (gu ? 2 : 1) * 128 * 128 * 4;
+}
+
 template <bool GU>
-__global__ void __launch_bounds__(256, 2) nv_gemm_kernel(int M, int K, int N, int ntm, int ntn,
+__global__ void __launch_bounds__(256, 2) nv_gemm_kernel(int M, int K, int N, NvPlan plan,
                                                         const uint16_t* __restrict__ a16,
                                                         const float* __restrict__ rowscale,
                                                         const uint8_t* __restrict__ w0, float inv0,
                                                         const uint8_t* __restrict__ w1, float inv1,
-                                                        void* __restrict__ out) {
+                                                        void* __restrict__ out, float* __restrict__ partials) {
   constexpr int NM = GU ? 2 : 1;
   constexpr int MB = kNvMB;
   constexpr int NW = NM * 5;                   // weight copies per wave per block: 288 chunks (+32 pad) per matrix
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  const int per = gridDim.x >> 3;
-  const int tile = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
-  if (tile >= ntm * ntn) return;
+  const int nk = K >> 6;
+  const int nblk = (nk + 3) >> 2;
+  // Workgroups [0, units_grid) run the K parts of the split tiles (dispatched first, so they finish
+  // early); the rest run whole tiles in an XCD-aware order: workgroup b runs on XCD b % 8, and each XCD
+  // gets a contiguous run of tiles (n fastest) so the activation band it works on stays in its L2.
+  const int b = (int)blockIdx.x;
+  int tile, part = -1, kb0 = 0, kb1 = nblk;
+  if (b < plan.units_grid) {
+    if (b >= plan.units) return;
+    tile = plan.full + b / plan.S;
+    part = b - (b / plan.S) * plan.S;
+    kb0 = part * plan.bps;
+    kb1 = min(kb0 + plan.bps, nblk);
+  } else {
+    const int f = b - plan.units_grid;
+    const int per = ((int)gridDim.x - plan.units_grid) >> 3;
+    tile = (f & 7) * per + (f >> 3);
+    if (tile >= plan.full) return;
+  }
+  const int kt0 = 4 * kb0, kt1 = min(4 * kb1, nk);
+  const int ntn = plan.ntn;
   const int tm = tile / ntn;
   const int tn = tile - tm * ntn;
   const int m0 = tm * 32 * MB;
@@ -328,8 +400,6 @@ __global__ void __launch_bounds__(256, 2) nv_gemm_kernel(int M, int K, int N, in
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 31;
   const int h = lane >> 5;
-  const int nk = K >> 6;
-  const int nblk = (nk + 3) >> 2;
   const uint32_t rb = (uint32_t)nk * 36u;      // bytes per weight row
   const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
   const uint32_t wlds = lds0 + 2 * kNvAStage + wave * nv_wave_wbytes(GU);
@@ -451,15 +521,15 @@ __global__ void __launch_bounds__(256, 2) nv_gemm_kernel(int M, int K, int N, in
 
   // Prologue: weight block 0, activation steps 0 and 1; wait for block 0 and step 0 (step 1 may fly),
   // read block 0 into registers and refill the buffer with block 1.
-  copy_w(0);
-  copy_a(0, 0);
-  copy_a(1, 1);
+  copy_w(kb0);
+  copy_a(kt0, 0);
+  copy_a(kt0 + 1, 1);
   wait_vmem<MB>();
   __syncthreads();
   WBlock wb[NM];
-  read_block(wb, 0);
+  read_block(wb, kb0);
   wait_lds();
-  copy_w(1);
+  copy_w(kb0 + 1);
   f16x8 af0[MB], af1[MB];
   read_a(0, 0, af0);
   // K step kt (stage kt & 1, record J of the block in registers).
@@ -490,13 +560,26 @@ __global__ void __launch_bounds__(256, 2) nv_gemm_kernel(int M, int K, int N, in
       copy_w((kt >> 2) + 2);
     }
   };
-  for (int kt = 0; kt < nk; kt += 4) {
+  for (int kt = kt0; kt < kt1; kt += 4) {     // kt0 is a multiple of 4: record J = kt % 4
     step(kt, std::integral_constant<int, 0>{});
-    if (kt + 1 < nk) step(kt + 1, std::integral_constant<int, 1>{});
-    if (kt + 2 < nk) step(kt + 2, std::integral_constant<int, 2>{});
-    if (kt + 3 < nk) step(kt + 3, std::integral_constant<int, 3>{});
+    if (kt + 1 < kt1) step(kt + 1, std::integral_constant<int, 1>{});
+    if (kt + 2 < kt1) step(kt + 2, std::integral_constant<int, 2>{});
+    if (kt + 3 < kt1) step(kt + 3, std::integral_constant<int, 3>{});
   }
   wait_vmem<0>();                            // the trailing (clamped) copies land before the LDS is released
+
+  if (part >= 0) {                           // raw partial tile [NM][128][128], finished by nv_splitk_finish
+    float* pt = partials + (size_t)b * NM * 16384;
+    const int col = 32 * wave + li;
+#pragma unroll
+    for (int t = 0; t < NM; ++t)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          pt[t * 16384 + (32 * mb + 8 * (r >> 2) + 4 * h + (r & 3)) * 128 + col] = acc[t][mb][r];
+    return;
+  }
 
   const int ncol = n0 + 32 * wave + li;
   if (ncol >= N) return;
@@ -520,9 +603,41 @@ __global__ void __launch_bounds__(256, 2) nv_gemm_kernel(int M, int K, int N, in
   }
 }
 
+// Epilogue of the split tiles: element (row, col) of split tile i adds its S parts in part order.
+template <bool GU>
+__global__ void __launch_bounds__(256) nv_splitk_finish(int M, int N, NvPlan plan, const float* __restrict__ partials,
+                                                       const float* __restrict__ rowscale, float inv0, float inv1,
+                                                       void* __restrict__ out) {
+  constexpr int NM = GU ? 2 : 1;
+  const int i = (int)blockIdx.x >> 6;                  // split tile index
+  const int e = ((int)blockIdx.x & 63) * 256 + (int)threadIdx.x;
+  const int tile = plan.full + i;
+  const int tm = tile / plan.ntn, tn = tile - tm * plan.ntn;
+  const int m = tm * 128 + (e >> 7), n = tn * 128 + (e & 127);
+  if (m >= M || n >= N) return;
+  const float* p = partials + (size_t)i * plan.S * NM * 16384 + e;
+  float acc[NM];
+#pragma unroll
+  for (int t = 0; t < NM; ++t) acc[t] = p[t * 16384];
+  for (int s = 1; s < plan.S; ++s)
+#pragma unroll
+    for (int t = 0; t < NM; ++t) acc[t] += p[(size_t)s * NM * 16384 + t * 16384];
+  const float rs = rowscale ? rowscale[m] : 1.0f;
+  if constexpr (GU) {
+    const float g = acc[0] * rs * inv0;
+    const float u = acc[1] * rs * inv1;
+    const _Float16 a = (_Float16)(silu_f32(g) * u);
+    reinterpret_cast<uint16_t*>(out)[(size_t)m * N + n] = __builtin_bit_cast(uint16_t, a);
+  } else {
+    reinterpret_cast<float*>(out)[(size_t)m * N + n] = acc[0] * rs * inv0;
+  }
+}
+
 template <bool GU>
 hipError_t nv_dispatch(int M, int K, int N, const uint16_t* a16, const float* rowscale, const uint8_t* w0,
-                       float inv0, const uint8_t* w1, float inv1, void* out, hipStream_t st) {
+                       float inv0, const uint8_t* w1, float inv1, void* out, float* partials, hipStream_t st) {
+  const NvPlan plan = nv_plan(M, K, N, GU);
+  if (plan.units > 0 && partials == nullptr) return hipErrorInvalidValue;
   // 72 KB (gate+up) / 52 KB of dynamic LDS: raise the per-kernel limit once per device
   static std::atomic<uint64_t> raised{0};
   int dev = 0;
@@ -535,11 +650,13 @@ hipError_t nv_dispatch(int M, int K, int N, const uint16_t* a16, const float* ro
     if (e != hipSuccess) return e;
     raised.fetch_or(bit);
   }
-  const int ntn = (N + 127) / 128;
-  const int ntm = (M + 32 * kNvMB - 1) / (32 * kNvMB);
-  const int grid = (ntm * ntn + 7) / 8 * 8;
-  hipLaunchKernelGGL((nv_gemm_kernel<GU>), dim3(grid), dim3(256), nv_lds_bytes(GU), st, M, K, N, ntm, ntn, a16,
-                     rowscale, w0, inv0, w1, inv1, out);
+  const int grid = plan.units_grid + (plan.full + 7) / 8 * 8;
+  hipLaunchKernelGGL((nv_gemm_kernel<GU>), dim3(grid), dim3(256), nv_lds_bytes(GU), st, M, K, N, plan, a16, rowscale,
+                     w0, inv0, w1, inv1, out, partials);
+  e = hipGetLastError();
+  if (e != hipSuccess || plan.units == 0) return e;
+  hipLaunchKernelGGL((nv_splitk_finish<GU>), dim3((plan.tiles - plan.full) * 64), dim3(256), 0, st, M, N, plan,
+                     partials, rowscale, inv0, inv1, out);
   return hipGetLastError();
 }
 
@@ -576,18 +693,25 @@ hipError_t launch_rowscale_f16(int M, int K, const void* x, XType xt, uint16_t* 
   return hipGetLastError();
 }
 
+size_t mfma_partial_bytes(int fmt, int M, int K, int N, bool gu) {
+  if (fmt != 1 || K < 256 || M <= 0) return 0;
+  return nv_partial_bytes(nv_plan(M, K, N, gu), gu);
+}
+
 hipError_t launch_mfma_gateup(int fmt, int M, int K, int N, const uint16_t* x16, const float* rowscale,
                               const uint8_t* w0, const float* cs0, float inv0, const uint8_t* w1,
-                              const float* cs1, float inv1, uint16_t* act16, hipStream_t st) {
-  if (fmt == 1 && K >= 256) return nv_dispatch<true>(M, K, N, x16, rowscale, w0, inv0, w1, inv1, act16, st);
+                              const float* cs1, float inv1, uint16_t* act16, float* partials, hipStream_t st) {
+  if (fmt == 1 && K >= 256)
+    return nv_dispatch<true>(M, K, N, x16, rowscale, w0, inv0, w1, inv1, act16, partials, st);
   if (fmt == 1)
     return gemm_dispatch<1, true>(M, K, N, x16, rowscale, w0, cs0, inv0, w1, cs1, inv1, act16, st);
   return gemm_dispatch<0, true>(M, K, N, x16, rowscale, w0, cs0, inv0, w1, cs1, inv1, act16, st);
 }
 
 hipError_t launch_mfma_linear(int fmt, int M, int K, int N, const uint16_t* a16, const float* rowscale,
-                              const uint8_t* w, const float* cs, float inv, float* y, hipStream_t st) {
-  if (fmt == 1 && K >= 256) return nv_dispatch<false>(M, K, N, a16, rowscale, w, inv, nullptr, 0.f, y, st);
+                              const uint8_t* w, const float* cs, float inv, float* y, float* partials,
+                              hipStream_t st) {
+  if (fmt == 1 && K >= 256) return nv_dispatch<false>(M, K, N, a16, rowscale, w, inv, nullptr, 0.f, y, partials, st);
   if (fmt == 1) return gemm_dispatch<1, false>(M, K, N, a16, rowscale, w, cs, inv, nullptr, nullptr, 0.f, y, st);
   return gemm_dispatch<0, false>(M, K, N, a16, rowscale, w, cs, inv, nullptr, nullptr, 0.f, y, st);
 }
