@@ -70,20 +70,64 @@ __device__ __forceinline__ float to_f32<float>(float v) { return v; }
 template <>
 __device__ __forceinline__ float to_f32<uint16_t>(uint16_t v) { return bf16_bits_to_f32(v); }
 
+// One wave per row: the row is read once in 16-byte chunks (8 bf16 or 4 float32 per chunk) and kept in
+// registers (up to RC chunks per lane; rows longer than 64*RC chunks re-read the rest from memory),
+// reduced to max |x| across the wave, then scaled and written as float16 chunks.
+// Power-of-two row scale e: max |x| * 2^-e lies in [2^14, 2^15).
 template <typename XT>
-__global__ void __launch_bounds__(256) rowscale_f16_kernel(int K, const XT* __restrict__ x,
+struct RowChunk;
+template <>
+struct RowChunk<uint16_t> {   // 8 bf16
+  static constexpr int E = 8;
+  static __device__ __forceinline__ void unpack(u32x4 v, float* f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(v[i] << 16);
+      f[2 * i + 1] = __uint_as_float(v[i] & 0xFFFF0000u);
+    }
+  }
+};
+template <>
+struct RowChunk<float> {      // 4 float32
+  static constexpr int E = 4;
+  static __device__ __forceinline__ void unpack(u32x4 v, float* f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(v[i]);
+  }
+};
+
+template <typename XT, int RC>
+__global__ void __launch_bounds__(256) rowscale_f16_kernel(int M, int K, const XT* __restrict__ x,
                                                            uint16_t* __restrict__ x16,
                                                            float* __restrict__ rowscale) {
-  __shared__ float red[4];
-  const size_t m = blockIdx.x;
-  const XT* xr = x + m * K;
+  constexpr int E = RowChunk<XT>::E;
+  const int m = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6);
+  if (m >= M) return;
+  const int lane = threadIdx.x & 63;
+  const int nch = K / E;                               // K is a multiple of 64
+  const u32x4* xr = reinterpret_cast<const u32x4*>(x + (size_t)m * K);
+  u32x4 cache[RC];
+#pragma unroll
+  for (int i = 0; i < RC; ++i) {
+    const int c = lane + 64 * i;
+    cache[i] = c < nch ? xr[c] : u32x4{0u, 0u, 0u, 0u};
+  }
   float amax = 0.f;
-  for (int k = threadIdx.x; k < K; k += 256) amax = fmaxf(amax, fabsf(to_f32<XT>(xr[k])));
+#pragma unroll
+  for (int i = 0; i < RC; ++i) {
+    float f[E];
+    RowChunk<XT>::unpack(cache[i], f);
+#pragma unroll
+    for (int j = 0; j < E; ++j) amax = fmaxf(amax, fabsf(f[j]));
+  }
+  for (int c = lane + 64 * RC; c < nch; c += 64) {
+    float f[E];
+    RowChunk<XT>::unpack(xr[c], f);
+#pragma unroll
+    for (int j = 0; j < E; ++j) amax = fmaxf(amax, fabsf(f[j]));
+  }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
-  __syncthreads();
-  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   int e = 0;
   if (amax > 0.f && amax <= 3.0e38f) {
     int ex;
@@ -91,12 +135,26 @@ __global__ void __launch_bounds__(256) rowscale_f16_kernel(int K, const XT* __re
     e = ex - 15;                // amax * 2^-e in [2^14, 2^15)
     e = e < -100 ? -100 : (e > 100 ? 100 : e);
   }
-  if (threadIdx.x == 0) rowscale[m] = ldexpf(1.0f, e);
-  uint16_t* o = x16 + m * K;
-  for (int k = threadIdx.x; k < K; k += 256) {
-    const _Float16 h = (_Float16)ldexpf(to_f32<XT>(xr[k]), -e);
-    o[k] = __builtin_bit_cast(uint16_t, h);
+  if (lane == 0) rowscale[m] = ldexpf(1.0f, e);
+  uint16_t* o = x16 + (size_t)m * K;
+  auto put = [&](int c, u32x4 v) {
+    float f[E];
+    RowChunk<XT>::unpack(v, f);
+    uint32_t h[E / 2];
+#pragma unroll
+    for (int j = 0; j < E / 2; ++j) {
+      const _Float16 lo = (_Float16)ldexpf(f[2 * j], -e), hi = (_Float16)ldexpf(f[2 * j + 1], -e);
+      h[j] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+    }
+    if constexpr (E == 8) reinterpret_cast<u32x4*>(o)[c] = u32x4{h[0], h[1], h[2], h[3]};
+    else reinterpret_cast<u32x2*>(o)[c] = u32x2{h[0], h[1]};
+  };
+#pragma unroll
+  for (int i = 0; i < RC; ++i) {
+    const int c = lane + 64 * i;
+    if (c < nch) put(c, cache[i]);
   }
+  for (int c = lane + 64 * RC; c < nch; c += 64) put(c, xr[c]);
 }
 
 // ---- the GEMM ------------------------------------------------------------------------------------
@@ -684,11 +742,13 @@ hipError_t gemm_dispatch(int M, int K, int N, const uint16_t* a16, const float* 
 
 hipError_t launch_rowscale_f16(int M, int K, const void* x, XType xt, uint16_t* x16, float* rowscale,
                                hipStream_t st) {
+  // four rows (waves) per workgroup; 10 (bf16) / 20 (float32) register chunks per lane cover K = 5120
+  const dim3 grid((M + 3) / 4);
   if (xt == X_BF16)
-    hipLaunchKernelGGL(rowscale_f16_kernel<uint16_t>, dim3(M), dim3(256), 0, st, K,
+    hipLaunchKernelGGL((rowscale_f16_kernel<uint16_t, 10>), grid, dim3(256), 0, st, M, K,
                        reinterpret_cast<const uint16_t*>(x), x16, rowscale);
   else
-    hipLaunchKernelGGL(rowscale_f16_kernel<float>, dim3(M), dim3(256), 0, st, K,
+    hipLaunchKernelGGL((rowscale_f16_kernel<float, 20>), grid, dim3(256), 0, st, M, K,
                        reinterpret_cast<const float*>(x), x16, rowscale);
   return hipGetLastError();
 }
