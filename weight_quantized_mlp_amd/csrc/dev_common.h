@@ -83,6 +83,32 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// Cross-lane sums through DPP (register-to-register, no LDS round trip).  row16_sum: the sum of each
+// 16-lane row in every lane of that row, built from lane^1, lane^2 (quad permutes), then the half-row
+// and row mirrors (which pair the already uniform quads and half rows).  wave64_sum: the four row
+// sums added as (r0 + r1) + (r2 + r3), the same wave-uniform value in every lane.  Fixed order, so
+// bitwise reproducible.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f32<0xB1>(v);    // quad_perm [1,0,3,2]
+  v += dpp_f32<0x4E>(v);    // quad_perm [2,3,0,1]
+  v += dpp_f32<0x141>(v);   // row_half_mirror
+  v += dpp_f32<0x140>(v);   // row_mirror
+  return v;
+}
+__device__ __forceinline__ float wave64_sum(float v) {
+  v = row16_sum(v);
+  const int b = __builtin_bit_cast(int, v);
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48));
+  return (r0 + r1) + (r2 + r3);
+}
+
 __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + expf(-z)); }
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }

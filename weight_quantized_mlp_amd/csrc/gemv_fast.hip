@@ -61,9 +61,9 @@ __device__ __forceinline__ u32x4 ld16a4(const uint8_t* p) {
 }
 template <int W>
 __device__ __forceinline__ float gsum(float v) {
-#pragma unroll
-  for (int o = W / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  static_assert(W == 64 || W == 16, "wave or row sum");
+  if constexpr (W == 64) return wave64_sum(v);
+  else return row16_sum(v);
 }
 __device__ __forceinline__ float e4m3_group(uint32_t d, int g) {
   return g == 0 ? e4m3_byte_f32<0>(d) : g == 1 ? e4m3_byte_f32<1>(d) : g == 2 ? e4m3_byte_f32<2>(d)
