@@ -78,8 +78,8 @@ int wq_last_hip_error(void);
  * invalid arguments or M == 0.
  *   GEMV path: act float32 [M, I].
  *   MFMA path: x as float16 [M, H] (row-scaled), per-row scales float32 [M],
- *              act float16 [M, I], then (NVFP4, M >= 128) float32 split-K
- *              partial tiles of at most 64 MiB; each region 256-byte aligned.
+ *              act float16 [M, I], then (NVFP4) float32 split-K partial
+ *              tiles of at most 64 MiB; each region 256-byte aligned.
  *              The size is a function of the shape alone.
  */
 size_t mlp_workspace_bytes(int fmt, int64_t M, int64_t H, int64_t I, int flags);

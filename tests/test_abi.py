@@ -54,7 +54,10 @@ def test_workspace_queries(L):
     n = wq.mlp_workspace_bytes(1, 512, 5120, 17408)
     assert n >= 512 * 5120 * 2 + 512 * 4 + 512 * 17408 * 2
     assert wq.mlp_workspace_bytes(1, 4, 5120, 17408, "gemv") == 4 * 17408 * 4
-    assert wq.mlp_workspace_bytes(1, 4, 5120, 17408, "mfma") == 4 * 5120 * 2 + 256 + 4 * 17408 * 2
+    # MFMA path: x16, row scales, act16, then (NVFP4) split-K partial tiles of at most 64 MiB
+    base = 4 * 5120 * 2 + 256 + 4 * 17408 * 2
+    assert wq.mlp_workspace_bytes(0, 4, 5120, 17408, "mfma") == base
+    assert base < wq.mlp_workspace_bytes(1, 4, 5120, 17408, "mfma") <= base + (64 << 20)
     assert wq.mlp_workspace_bytes(7, 1, 64, 64) == 0
     assert wq.mlp_workspace_bytes(0, 0, 64, 64) == 0
     assert wq.qlinear_workspace_bytes(1, 4, 64, 64) == 0

@@ -1,4 +1,4 @@
-// M >= 128 path: LDS-tiled MFMA GEMMs with in-kernel weight decode (gfx950).
+// MFMA path: LDS-tiled MFMA GEMMs with in-kernel weight decode (gfx950).
 //
 // Method: issue "tp>1 fp8w tail-MLP shard host-dequantizes every layer", section
 // "Proposed fix" (SwiGLU MLP); NVFP4 numerics and the 36-byte record from page
@@ -35,7 +35,9 @@
 // a block each wave reads the whole block of its columns into registers and immediately refills the
 // buffer with the next block, so the weight copy has four K steps to land.  Inside a K step the
 // activation fragments of sub-step s+1 are read while the MFMAs of sub-step s run; the single barrier
-// per K step sits after the third sub-step.  Two workgroups share a CU (72 KB of LDS each).
+// per K step sits after the third sub-step.  Two workgroups share a CU (at most 72 KB of LDS each).
+// Batches of at most 32 or 64 rows run 32- or 64-row tiles (MB = 1, 2), so a short batch streams the
+// weights once with little padding; the split-K plan below then spreads the few tiles over the chip.
 //
 // MFMA v_mfma_f32_32x32x16_f16 operand layout (checked on gfx950): A lane l holds row
 // l%32, k = 8*(l/32) + j; B lane l holds column l%32, same k; D register r of lane l
@@ -359,12 +361,13 @@ __device__ __forceinline__ void wait_vmem() {
 }
 __device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }   // lgkmcnt(0)
 
-constexpr int kNvMB = 4;                       // 128-row tiles
-constexpr int kNvAStage = 32 * kNvMB * 128;    // bytes per activation stage
+// MB = 1, 2, 4: 32-, 64- or 128-row tiles (the narrow ones for M < 97)
+constexpr int nv_astage(int mb) { return 32 * mb * 128; }   // bytes per activation stage
 constexpr int nv_wave_wbytes(bool gu) { return (gu ? 2 : 1) * 5 * 1024; }
-constexpr int nv_lds_bytes(bool gu) { return 2 * kNvAStage + 4 * nv_wave_wbytes(gu); }
+constexpr int nv_lds_bytes(bool gu, int mb) { return 2 * nv_astage(mb) + 4 * nv_wave_wbytes(gu); }
+inline int nv_mb(int M) { return M <= 32 ? 1 : (M <= 64 ? 2 : 4); }
 
-// Work plan of one launch, a pure function of the shape.  128x128 tiles; with two workgroups on each
+// Work plan of one launch, a pure function of the shape.  (32*MB)x128 tiles; with two workgroups on each
 // of the 256 CUs there are 512 slots.  When the last round of tiles would leave most slots idle (or
 // there are fewer tiles than slots at all) the tiles of that round are split along K into S parts of
 // whole 4-record weight blocks: the parts run first, store raw float32 partial tiles, and a second
@@ -373,6 +376,7 @@ constexpr int nv_lds_bytes(bool gu) { return 2 * kNvAStage + 4 * nv_wave_wbytes(
 constexpr int kNvSlots = 512;
 constexpr size_t kNvMaxPartials = (size_t)64 << 20;
 struct NvPlan {
+  int bm;                // tile rows: 32 * MB
   int ntm, ntn, tiles;   // tile grid
   int full;              // tiles [0, full) run whole
   int S, bps;            // split tiles [full, tiles) run as S parts of bps blocks (S = 1: none)
@@ -380,12 +384,13 @@ struct NvPlan {
 };
 inline NvPlan nv_plan(int M, int K, int N, bool gu) {
   NvPlan p{};
-  p.ntm = (M + 127) / 128;
+  p.bm = 32 * nv_mb(M);
+  p.ntm = (M + p.bm - 1) / p.bm;
   p.ntn = (N + 127) / 128;
   p.tiles = p.ntm * p.ntn;
   const int nblk = (K / 64 + 3) / 4;
   int tail = 0;
-  if (M >= 128) {
+  {
     if (p.tiles < kNvSlots) {
       tail = p.tiles;
     } else {
@@ -397,7 +402,7 @@ inline NvPlan nv_plan(int M, int K, int N, bool gu) {
   // S minimises the rounds of parts per tile, ceil(tail * S / slots) / S (ties: fewer parts)
   int S = 1;
   if (tail > 0) {
-    const size_t per_part = (size_t)(gu ? 2 : 1) * 128 * 128 * 4;
+    const size_t per_part = (size_t)(gu ? 2 : 1) * p.bm * 128 * 4;
     double best = 1.0;
     for (int s = 2; s <= std::min(8, nblk); ++s) {
       if ((size_t)tail * s * per_part > kNvMaxPartials) break;
@@ -414,10 +419,10 @@ inline NvPlan nv_plan(int M, int K, int N, bool gu) {
   return p;
 }
 inline size_t nv_partial_bytes(const NvPlan& p, bool gu) {
-  return (size_t)p.units * (gu ? 2 : 1) * 128 * 128 * 4;
+  return (size_t)p.units * (gu ? 2 : 1) * p.bm * 128 * 4;
 }
 
-template <bool GU>
+template <bool GU, int MB>
 __global__ void __launch_bounds__(256, 2) nv_gemm_kernel(int M, int K, int N, NvPlan plan,
                                                         const uint16_t* __restrict__ a16,
                                                         const float* __restrict__ rowscale,
@@ -425,7 +430,8 @@ __global__ void __launch_bounds__(256, 2) nv_gemm_kernel(int M, int K, int N, Nv
                                                         const uint8_t* __restrict__ w1, float inv1,
                                                         void* __restrict__ out, float* __restrict__ partials) {
   constexpr int NM = GU ? 2 : 1;
-  constexpr int MB = kNvMB;
+  constexpr int kNvAStage = nv_astage(MB);
+  constexpr int PT = 32 * MB * 128;            // elements of one partial tile per matrix
   constexpr int NW = NM * 5;                   // weight copies per wave per block: 288 chunks (+32 pad) per matrix
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int nk = K >> 6;
@@ -627,7 +633,7 @@ __global__ void __launch_bounds__(256, 2) nv_gemm_kernel(int M, int K, int N, Nv
   wait_vmem<0>();                            // the trailing (clamped) copies land before the LDS is released
 
   if (part >= 0) {                           // raw partial tile [NM][128][128], finished by nv_splitk_finish
-    float* pt = partials + (size_t)b * NM * 16384;
+    float* pt = partials + (size_t)b * NM * PT;
     const int col = 32 * wave + li;
 #pragma unroll
     for (int t = 0; t < NM; ++t)
@@ -635,7 +641,7 @@ __global__ void __launch_bounds__(256, 2) nv_gemm_kernel(int M, int K, int N, Nv
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          pt[t * 16384 + (32 * mb + 8 * (r >> 2) + 4 * h + (r & 3)) * 128 + col] = acc[t][mb][r];
+          pt[t * PT + (32 * mb + 8 * (r >> 2) + 4 * h + (r & 3)) * 128 + col] = acc[t][mb][r];
     return;
   }
 
@@ -662,24 +668,27 @@ __global__ void __launch_bounds__(256, 2) nv_gemm_kernel(int M, int K, int N, Nv
 }
 
 // Epilogue of the split tiles: element (row, col) of split tile i adds its S parts in part order.
+// Workgroup b handles 256 elements of split tile b / (bm / 2) (a tile has bm * 128 elements).
 template <bool GU>
 __global__ void __launch_bounds__(256) nv_splitk_finish(int M, int N, NvPlan plan, const float* __restrict__ partials,
                                                        const float* __restrict__ rowscale, float inv0, float inv1,
                                                        void* __restrict__ out) {
   constexpr int NM = GU ? 2 : 1;
-  const int i = (int)blockIdx.x >> 6;                  // split tile index
-  const int e = ((int)blockIdx.x & 63) * 256 + (int)threadIdx.x;
+  const int per_tile = plan.bm / 2;                    // workgroups per split tile
+  const int i = (int)blockIdx.x / per_tile;            // split tile index
+  const int e = ((int)blockIdx.x - i * per_tile) * 256 + (int)threadIdx.x;
+  const int pt = plan.bm * 128;
   const int tile = plan.full + i;
   const int tm = tile / plan.ntn, tn = tile - tm * plan.ntn;
-  const int m = tm * 128 + (e >> 7), n = tn * 128 + (e & 127);
+  const int m = tm * plan.bm + (e >> 7), n = tn * 128 + (e & 127);
   if (m >= M || n >= N) return;
-  const float* p = partials + (size_t)i * plan.S * NM * 16384 + e;
+  const float* p = partials + (size_t)i * plan.S * NM * pt + e;
   float acc[NM];
 #pragma unroll
-  for (int t = 0; t < NM; ++t) acc[t] = p[t * 16384];
+  for (int t = 0; t < NM; ++t) acc[t] = p[t * pt];
   for (int s = 1; s < plan.S; ++s)
 #pragma unroll
-    for (int t = 0; t < NM; ++t) acc[t] += p[(size_t)s * NM * 16384 + t * 16384];
+    for (int t = 0; t < NM; ++t) acc[t] += p[(size_t)s * NM * pt + t * pt];
   const float rs = rowscale ? rowscale[m] : 1.0f;
   if constexpr (GU) {
     const float g = acc[0] * rs * inv0;
@@ -691,30 +700,42 @@ __global__ void __launch_bounds__(256) nv_splitk_finish(int M, int N, NvPlan pla
   }
 }
 
-template <bool GU>
-hipError_t nv_dispatch(int M, int K, int N, const uint16_t* a16, const float* rowscale, const uint8_t* w0,
-                       float inv0, const uint8_t* w1, float inv1, void* out, float* partials, hipStream_t st) {
-  const NvPlan plan = nv_plan(M, K, N, GU);
-  if (plan.units > 0 && partials == nullptr) return hipErrorInvalidValue;
-  // 72 KB (gate+up) / 52 KB of dynamic LDS: raise the per-kernel limit once per device
+template <bool GU, int MB>
+hipError_t nv_launch(int M, int K, int N, const NvPlan& plan, const uint16_t* a16, const float* rowscale,
+                     const uint8_t* w0, float inv0, const uint8_t* w1, float inv1, void* out, float* partials,
+                     hipStream_t st) {
+  // up to 72 KB of dynamic LDS: raise the per-kernel limit once per device
   static std::atomic<uint64_t> raised{0};
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   const uint64_t bit = (uint64_t)1 << (dev & 63);
   if (!(raised.load() & bit)) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(nv_gemm_kernel<GU>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, nv_lds_bytes(GU));
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(nv_gemm_kernel<GU, MB>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, nv_lds_bytes(GU, MB));
     if (e != hipSuccess) return e;
     raised.fetch_or(bit);
   }
   const int grid = plan.units_grid + (plan.full + 7) / 8 * 8;
-  hipLaunchKernelGGL((nv_gemm_kernel<GU>), dim3(grid), dim3(256), nv_lds_bytes(GU), st, M, K, N, plan, a16, rowscale,
-                     w0, inv0, w1, inv1, out, partials);
-  e = hipGetLastError();
+  hipLaunchKernelGGL((nv_gemm_kernel<GU, MB>), dim3(grid), dim3(256), nv_lds_bytes(GU, MB), st, M, K, N, plan, a16,
+                     rowscale, w0, inv0, w1, inv1, out, partials);
+  return hipGetLastError();
+}
+
+template <bool GU>
+hipError_t nv_dispatch(int M, int K, int N, const uint16_t* a16, const float* rowscale, const uint8_t* w0,
+                       float inv0, const uint8_t* w1, float inv1, void* out, float* partials, hipStream_t st) {
+  const NvPlan plan = nv_plan(M, K, N, GU);
+  if (plan.units > 0 && partials == nullptr) return hipErrorInvalidValue;
+  hipError_t e;
+  switch (plan.bm) {
+    case 32: e = nv_launch<GU, 1>(M, K, N, plan, a16, rowscale, w0, inv0, w1, inv1, out, partials, st); break;
+    case 64: e = nv_launch<GU, 2>(M, K, N, plan, a16, rowscale, w0, inv0, w1, inv1, out, partials, st); break;
+    default: e = nv_launch<GU, 4>(M, K, N, plan, a16, rowscale, w0, inv0, w1, inv1, out, partials, st); break;
+  }
   if (e != hipSuccess || plan.units == 0) return e;
-  hipLaunchKernelGGL((nv_splitk_finish<GU>), dim3((plan.tiles - plan.full) * 64), dim3(256), 0, st, M, N, plan,
-                     partials, rowscale, inv0, inv1, out);
+  hipLaunchKernelGGL((nv_splitk_finish<GU>), dim3((plan.tiles - plan.full) * (plan.bm / 2)), dim3(256), 0, st, M, N,
+                     plan, partials, rowscale, inv0, inv1, out);
   return hipGetLastError();
 }
 
