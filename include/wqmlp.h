@@ -53,7 +53,12 @@ enum {
   WQ_EWORKSPACE = -6, /* workspace missing or smaller than the query returns */
   WQ_ELAUNCH = -7     /* kernel launch failed; see wq_last_hip_error() */
 };
-/* path selection (flags bits 0-1): AUTO picks the MFMA GEMM for M >= WQ_MFMA_MIN_ROWS */
+/* path selection (flags bits 0-1).  AUTO picks the MFMA GEMM for M >= WQ_MFMA_MIN_ROWS, and for
+ * 1 < M < WQ_MFMA_MIN_ROWS when M >= WQ_NARROW_MIN_ROWS_NVFP4 / WQ_NARROW_MIN_ROWS_FP8 (by format), the
+ * call's weights (all matrices) hold at least WQ_NARROW_MIN_WEIGHT_BYTES and both dimensions are
+ * multiples of 64; otherwise the GEMV.  The thresholds are the measured crossovers of the two paths
+ * at hidden 5120, intermediate 17408 on MI355X (the GEMV streams the weights once per row, the GEMM
+ * once per call). */
 enum { WQ_PATH_AUTO = 0, WQ_PATH_GEMV = 1, WQ_PATH_MFMA = 2 };
 /* stage selection (flags bits 2-3, MLP entry points only; default: both stages).
  * GATEUP_ONLY enqueues the gate/up projection + SwiGLU, leaving act in the
@@ -62,6 +67,9 @@ enum { WQ_PATH_AUTO = 0, WQ_PATH_GEMV = 1, WQ_PATH_MFMA = 2 };
  * that interleave work or timing between the two stages. */
 enum { WQ_STAGE_GATEUP_ONLY = 4, WQ_STAGE_DOWN_ONLY = 8 };
 #define WQ_MFMA_MIN_ROWS 128
+#define WQ_NARROW_MIN_ROWS_NVFP4 3
+#define WQ_NARROW_MIN_ROWS_FP8 13
+#define WQ_NARROW_MIN_WEIGHT_BYTES (16u << 20)
 /* largest top-k the routed-expert step accepts */
 #define WQ_MOE_MAX_TOPK 16
 
@@ -96,10 +104,11 @@ size_t mlp_workspace_bytes(int fmt, int64_t M, int64_t H, int64_t I, int flags);
  *   out     [M, H]  float32
  * flags: WQ_PATH_* | optional WQ_STAGE_* bit.
  * Shapes: H, I > 0 and multiples of 16 (GEMV) or 64 (MFMA).  Accumulation is
- * float32; silu(z) = z / (1 + exp(-z)).  The GEMV path (M < 128 under AUTO)
- * reduces each output over k in a fixed order that does not depend on M, so
- * results are bitwise reproducible and row m of an M-row call equals a
- * 1-row call on row m.
+ * float32; silu(z) = z / (1 + exp(-z)).  The GEMV path (WQ_PATH_GEMV, or AUTO
+ * below the row thresholds above) reduces each output over k in a fixed order
+ * that does not depend on M, so results are bitwise reproducible and row m of
+ * an M-row call equals a 1-row call on row m.  The MFMA path is reproducible
+ * for a given shape; its split-K plan, and so its rounding, depends on M.
  */
 int mlp_fp8w_run(int64_t M, int64_t H, int64_t I, const void* x, int x_dtype,
                  const uint8_t* w_gate, const float* s_gate,

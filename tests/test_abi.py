@@ -58,6 +58,16 @@ def test_workspace_queries(L):
     base = 4 * 5120 * 2 + 256 + 4 * 17408 * 2
     assert wq.mlp_workspace_bytes(0, 4, 5120, 17408, "mfma") == base
     assert base < wq.mlp_workspace_bytes(1, 4, 5120, 17408, "mfma") <= base + (64 << 20)
+    # AUTO on short batches: the MFMA GEMM from the format's row threshold, for large weights only
+    gemv = lambda M, I: M * I * 4
+    assert wq.mlp_workspace_bytes(1, 2, 5120, 17408) == gemv(2, 17408)
+    assert wq.mlp_workspace_bytes(1, 3, 5120, 17408) == wq.mlp_workspace_bytes(1, 3, 5120, 17408, "mfma")
+    assert wq.mlp_workspace_bytes(0, 12, 5120, 17408) == gemv(12, 17408)
+    assert wq.mlp_workspace_bytes(0, 13, 5120, 17408) == wq.mlp_workspace_bytes(0, 13, 5120, 17408, "mfma")
+    assert wq.mlp_workspace_bytes(1, 64, 256, 512) == gemv(64, 512)           # 0.2 MB of weights
+    assert wq.mlp_workspace_bytes(0, 64, 5120 + 16, 17408) == gemv(64, 17408)   # H not a multiple of 64
+    assert wq.qlinear_workspace_bytes(1, 2, 5120, 17408) == 0
+    assert wq.qlinear_workspace_bytes(1, 3, 5120, 17408) > 0
     assert wq.mlp_workspace_bytes(7, 1, 64, 64) == 0
     assert wq.mlp_workspace_bytes(0, 0, 64, 64) == 0
     assert wq.qlinear_workspace_bytes(1, 4, 64, 64) == 0

@@ -137,14 +137,34 @@ def test_nvfp4_prefill_M8192_sampled(nv_big):
     assert np.all(np.isfinite(y))
 
 
-@pytest.mark.parametrize("M", [2, 37, 127, 128, 200])
+# M spans the short-batch tiles of the MFMA path: 32-row tiles with the block schedule (M <= 32 for
+# gate/up, M <= 128 for down, 1..4 row tiles), 64- and 128-row stepped tiles, split-K at every size.
+@pytest.mark.parametrize("M", [2, 3, 8, 17, 32, 37, 64, 96, 127, 128, 200])
 def test_nvfp4_paths_agree_with_oracle(nv_big, M):
     blk, gs, W, dblk = nv_big
     xb, _ = synth.nvfp4_x(M, outlier_frac=0.05)
     ref = nv_ref(W, oracle.bf16_bits_to_f64(xb))
+    ys = {}
     for path in ("gemv", "mfma"):
-        y = host(nv_run(dblk, gs, bf16_dev(xb), path=path))
-        gate(y, ref, what=f"nvfp4 M={M} {path}")
+        ys[path] = host(nv_run(dblk, gs, bf16_dev(xb), path=path))
+        gate(ys[path], ref, what=f"nvfp4 M={M} {path}")
+    # AUTO takes the GEMV below WQ_NARROW_MIN_ROWS_NVFP4 rows and the MFMA GEMM from there on
+    want = "gemv" if M < 3 else "mfma"
+    assert np.array_equal(host(nv_run(dblk, gs, bf16_dev(xb))).view(np.uint32), ys[want].view(np.uint32))
+
+
+@pytest.mark.parametrize("M", [12, 16, 48])
+def test_fp8_short_batch_paths_agree_with_oracle(fp8_big, M):
+    d = fp8_big
+    xb = synth.to_bf16_bits(np.random.default_rng(500 + M).standard_normal((M, 5120)).astype(np.float32))
+    ref = oracle.mlp_fp8w_ref(oracle.bf16_bits_to_f64(xb), *(d[n] for n in FP8_NAMES))
+    W = fp8_dev(d)
+    ys = {}
+    for path in ("gemv", "mfma"):
+        ys[path] = host(wq.mlp_fp8w_run(bf16_dev(xb), *W, path=path))
+        gate(ys[path], ref, what=f"fp8 M={M} {path}")
+    want = "gemv" if M < 13 else "mfma"                      # WQ_NARROW_MIN_ROWS_FP8
+    assert np.array_equal(host(wq.mlp_fp8w_run(bf16_dev(xb), *W)).view(np.uint32), ys[want].view(np.uint32))
 
 
 # ---- ragged tails: partial m and n tiles ----------------------------------------------------------------

@@ -108,16 +108,29 @@ bool gemv_fits(int fmt, int64_t K, int dt) {
   return per_row <= 160 * 1024;
 }
 
-int pick_path(int64_t M, int flags) {
-  flags &= 3;
-  if (flags == WQ_PATH_GEMV || flags == WQ_PATH_MFMA) return flags;
-  return M >= WQ_MFMA_MIN_ROWS ? WQ_PATH_MFMA : WQ_PATH_GEMV;
-}
-
 constexpr int64_t kMaxDim = (int64_t)1 << 30;
 
 size_t wbytes(int fmt, int64_t N, int64_t K) {
   return fmt == WQ_FMT_FP8W ? (size_t)N * (size_t)K : (size_t)N * (size_t)(K / 64) * 36;
+}
+
+// AUTO: the MFMA GEMM for M >= WQ_MFMA_MIN_ROWS, and for shorter batches of at least the format's
+// WQ_NARROW_MIN_ROWS_* rows when the call's weights hold at least WQ_NARROW_MIN_WEIGHT_BYTES and both
+// dimensions are multiples of 64 (the GEMV streams the weights once per row; the GEMM once per call).
+// wb: weight bytes of the call (all matrices).
+int pick_path(int fmt, int64_t M, int64_t D0, int64_t D1, size_t wb, int flags) {
+  flags &= 3;
+  if (flags == WQ_PATH_GEMV || flags == WQ_PATH_MFMA) return flags;
+  if (M >= WQ_MFMA_MIN_ROWS) return WQ_PATH_MFMA;
+  const int64_t narrow = fmt == WQ_FMT_NVFP4 ? WQ_NARROW_MIN_ROWS_NVFP4 : WQ_NARROW_MIN_ROWS_FP8;
+  if (M >= narrow && wb >= (size_t)WQ_NARROW_MIN_WEIGHT_BYTES && D0 % 64 == 0 && D1 % 64 == 0) return WQ_PATH_MFMA;
+  return WQ_PATH_GEMV;
+}
+int mlp_path(int fmt, int64_t M, int64_t H, int64_t I, int flags) {
+  return pick_path(fmt, M, H, I, 2 * wbytes(fmt, I, H) + wbytes(fmt, H, I), flags);
+}
+int linear_path(int fmt, int64_t M, int64_t N, int64_t K, int flags) {
+  return pick_path(fmt, M, N, K, wbytes(fmt, N, K), flags);
 }
 
 // Split-K scratch of the MFMA path: gate+up and down run one after the other and share it.
@@ -130,7 +143,7 @@ size_t mlp_partials(int fmt, int64_t M, int64_t H, int64_t I) {
 // Workspace of the two-layer MLP; 0 means "invalid".
 size_t mlp_ws(int fmt, int64_t M, int64_t H, int64_t I, int flags) {
   if (M <= 0 || H <= 0 || I <= 0 || M > kMaxDim || H > kMaxDim || I > kMaxDim) return 0;
-  if (pick_path(M, flags) == WQ_PATH_GEMV) return align256((size_t)M * I * 4);
+  if (mlp_path(fmt, M, H, I, flags) == WQ_PATH_GEMV) return align256((size_t)M * I * 4);
   return align256((size_t)M * H * 2) + align256((size_t)M * 4) + align256((size_t)M * I * 2) +
          align256(mlp_partials(fmt, M, H, I));
 }
@@ -155,7 +168,8 @@ int mlp_run(int fmt, int64_t M, int64_t H, int64_t I, const void* x, int x_dtype
   const bool do_gu = stage != WQ_STAGE_DOWN_ONLY, do_down = stage != WQ_STAGE_GATEUP_ONLY;
   if (x_dtype != WQ_F32 && x_dtype != WQ_BF16) return WQ_EINVAL;
   if (M < 0 || M > kMaxDim) return WQ_EINVAL;
-  const int path = pick_path(M, flags);
+  if (H <= 0 || I <= 0 || H > kMaxDim || I > kMaxDim) return WQ_EINVAL;
+  const int path = mlp_path(fmt, M, H, I, flags);
   if (!shape_ok(fmt, path, H, I, x_dtype)) return WQ_EINVAL;
   if (any_null({x, wg, wu, wd, out})) return WQ_EINVAL;
   if (fmt == WQ_FMT_FP8W && any_null({sg, su, sd})) return WQ_EINVAL;
@@ -348,7 +362,7 @@ int awq_dequant_f16(int64_t E, int64_t N, int64_t K, const void* bank, int meta_
 size_t qlinear_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K, int flags) {
   if ((fmt != WQ_FMT_FP8W && fmt != WQ_FMT_NVFP4) || flags < WQ_PATH_AUTO || flags > WQ_PATH_MFMA) return 0;
   if (M <= 0 || N <= 0 || K <= 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return 0;
-  if (pick_path(M, flags) == WQ_PATH_GEMV) return 0;
+  if (linear_path(fmt, M, N, K, flags) == WQ_PATH_GEMV) return 0;
   return align256((size_t)M * K * 2) + align256((size_t)M * 4) +
          align256(wq::mfma_partial_bytes(fmt == WQ_FMT_NVFP4 ? 1 : 0, (int)M, (int)K, (int)N, false));
 }
@@ -360,7 +374,7 @@ int qlinear_run(int fmt, int64_t M, int64_t N, int64_t K, const void* x, int x_d
   if (flags < WQ_PATH_AUTO || flags > WQ_PATH_MFMA) return WQ_EINVAL;
   if (x_dtype != WQ_F32 && x_dtype != WQ_BF16) return WQ_EINVAL;
   if (M < 0 || M > kMaxDim || N <= 0 || K <= 0 || N > kMaxDim || K > kMaxDim) return WQ_EINVAL;
-  const int path = pick_path(M, flags);
+  const int path = linear_path(fmt, M, N, K, flags);
   if (path == WQ_PATH_MFMA || fmt == WQ_FMT_NVFP4) {
     if (N % 64 || K % 64) return WQ_EINVAL;
   } else if (N % 16 || K % 16) {

@@ -38,6 +38,8 @@
 // per K step sits after the third sub-step.  Two workgroups share a CU (at most 72 KB of LDS each).
 // Batches of at most 32 or 64 rows run 32- or 64-row tiles (MB = 1, 2), so a short batch streams the
 // weights once with little padding; the split-K plan below then spreads the few tiles over the chip.
+// A 32-row tile's K step is too short to cover a memory round trip, so those tiles copy the
+// activations of a whole 4-record block with its weights and wait once per block (block schedule).
 //
 // MFMA v_mfma_f32_32x32x16_f16 operand layout (checked on gfx950): A lane l holds row
 // l%32, k = 8*(l/32) + j; B lane l holds column l%32, same k; D register r of lane l
@@ -364,8 +366,16 @@ __device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F);
 // MB = 1, 2, 4: 32-, 64- or 128-row tiles (the narrow ones for M < 97)
 constexpr int nv_astage(int mb) { return 32 * mb * 128; }   // bytes per activation stage
 constexpr int nv_wave_wbytes(bool gu) { return (gu ? 2 : 1) * 5 * 1024; }
-constexpr int nv_lds_bytes(bool gu, int mb) { return 2 * nv_astage(mb) + 4 * nv_wave_wbytes(gu); }
-inline int nv_mb(int M) { return M <= 32 ? 1 : (M <= 64 ? 2 : 4); }
+// Activation stages in the LDS ring: 2 (one per K step, stepped schedule) or 8 (two 4-step blocks,
+// block schedule)
+constexpr int nv_astages(bool bs) { return bs ? 8 : 2; }
+constexpr int nv_lds_bytes(bool gu, int mb, bool bs) { return nv_astages(bs) * nv_astage(mb) + 4 * nv_wave_wbytes(gu); }
+// Tile rows / 32 for an M-row launch.  The down projection (long K, short N) keeps 32-row tiles up to
+// M = 128: re-reading its weights once per 32 rows costs less than the stepped schedule's waits.
+inline int nv_mb(int M, bool gu) {
+  if (!gu && M <= 128) return 1;
+  return M <= 32 ? 1 : (M <= 64 ? 2 : 4);
+}
 
 // Work plan of one launch, a pure function of the shape.  (32*MB)x128 tiles; with two workgroups on each
 // of the 256 CUs there are 512 slots.  When the last round of tiles would leave most slots idle (or
@@ -382,21 +392,22 @@ struct NvPlan {
   int S, bps;            // split tiles [full, tiles) run as S parts of bps blocks (S = 1: none)
   int units, units_grid; // (tiles - full) * S parts; rounded up to a multiple of 8
 };
-inline NvPlan nv_plan(int M, int K, int N, bool gu) {
+// slots: concurrent workgroups; smax: most K parts per tile; mb: tile rows / 32 (0: nv_mb(M))
+inline NvPlan nv_plan_ex(int M, int K, int N, bool gu, int slots, int smax, int mb = 0) {
   NvPlan p{};
-  p.bm = 32 * nv_mb(M);
+  p.bm = 32 * (mb > 0 ? mb : nv_mb(M, gu));
   p.ntm = (M + p.bm - 1) / p.bm;
   p.ntn = (N + 127) / 128;
   p.tiles = p.ntm * p.ntn;
   const int nblk = (K / 64 + 3) / 4;
   int tail = 0;
   {
-    if (p.tiles < kNvSlots) {
+    if (p.tiles < slots) {
       tail = p.tiles;
     } else {
-      const int rounds = (p.tiles + kNvSlots - 1) / kNvSlots;
-      tail = p.tiles - (rounds - 1) * kNvSlots;
-      if (tail * 10 >= kNvSlots * 9) tail = 0;   // a nearly full last round runs whole
+      const int rounds = (p.tiles + slots - 1) / slots;
+      tail = p.tiles - (rounds - 1) * slots;
+      if (tail * 10 >= slots * 9) tail = 0;   // a nearly full last round runs whole
     }
   }
   // S minimises the rounds of parts per tile, ceil(tail * S / slots) / S (ties: fewer parts)
@@ -404,9 +415,9 @@ inline NvPlan nv_plan(int M, int K, int N, bool gu) {
   if (tail > 0) {
     const size_t per_part = (size_t)(gu ? 2 : 1) * p.bm * 128 * 4;
     double best = 1.0;
-    for (int s = 2; s <= std::min(8, nblk); ++s) {
+    for (int s = 2; s <= std::min(smax, nblk); ++s) {
       if ((size_t)tail * s * per_part > kNvMaxPartials) break;
-      const double t = (double)((tail * s + kNvSlots - 1) / kNvSlots) / s;
+      const double t = (double)((tail * s + slots - 1) / slots) / s;
       if (t < best - 1e-9) { best = t; S = s; }
     }
   }
@@ -418,11 +429,12 @@ inline NvPlan nv_plan(int M, int K, int N, bool gu) {
   p.units_grid = (p.units + 7) / 8 * 8;
   return p;
 }
+inline NvPlan nv_plan(int M, int K, int N, bool gu) { return nv_plan_ex(M, K, N, gu, kNvSlots, 8); }
 inline size_t nv_partial_bytes(const NvPlan& p, bool gu) {
   return (size_t)p.units * (gu ? 2 : 1) * p.bm * 128 * 4;
 }
 
-template <bool GU, int MB>
+template <bool GU, int MB, bool BS>
 __global__ void __launch_bounds__(256, 2) nv_gemm_kernel(int M, int K, int N, NvPlan plan,
                                                         const uint16_t* __restrict__ a16,
                                                         const float* __restrict__ rowscale,
@@ -431,6 +443,7 @@ __global__ void __launch_bounds__(256, 2) nv_gemm_kernel(int M, int K, int N, Nv
                                                         void* __restrict__ out, float* __restrict__ partials) {
   constexpr int NM = GU ? 2 : 1;
   constexpr int kNvAStage = nv_astage(MB);
+  constexpr int AS = nv_astages(BS);
   constexpr int PT = 32 * MB * 128;            // elements of one partial tile per matrix
   constexpr int NW = NM * 5;                   // weight copies per wave per block: 288 chunks (+32 pad) per matrix
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -466,8 +479,8 @@ __global__ void __launch_bounds__(256, 2) nv_gemm_kernel(int M, int K, int N, Nv
   const int h = lane >> 5;
   const uint32_t rb = (uint32_t)nk * 36u;      // bytes per weight row
   const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
-  const uint32_t wlds = lds0 + 2 * kNvAStage + wave * nv_wave_wbytes(GU);
-  const uint8_t* wbuf = lds + 2 * kNvAStage + wave * nv_wave_wbytes(GU);
+  const uint32_t wlds = lds0 + AS * kNvAStage + wave * nv_wave_wbytes(GU);
+  const uint8_t* wbuf = lds + AS * kNvAStage + wave * nv_wave_wbytes(GU);
 
   // Activation chunk p = tid + 256 i: tile row p >> 3, LDS chunk p & 7, global chunk (p & 7) ^ (row & 7).
   uint32_t aoff[MB];
@@ -505,6 +518,7 @@ __global__ void __launch_bounds__(256, 2) nv_gemm_kernel(int M, int K, int N, Nv
     for (int j = 0; j < NW; ++j)
       lds_copy16(woff[j] + boff, j < 5 ? w0 : w1, __builtin_amdgcn_readfirstlane(wlds + 1024 * j));
   };
+
   f32x16 acc[NM][MB];
 #pragma unroll
   for (int t = 0; t < NM; ++t)
@@ -583,56 +597,113 @@ __global__ void __launch_bounds__(256, 2) nv_gemm_kernel(int M, int K, int N, Nv
     }
   };
 
-  // Prologue: weight block 0, activation steps 0 and 1; wait for block 0 and step 0 (step 1 may fly),
-  // read block 0 into registers and refill the buffer with block 1.
-  copy_w(kb0);
-  copy_a(kt0, 0);
-  copy_a(kt0 + 1, 1);
-  wait_vmem<MB>();
-  __syncthreads();
   WBlock wb[NM];
-  read_block(wb, kb0);
-  wait_lds();
-  copy_w(kb0 + 1);
   f16x8 af0[MB], af1[MB];
-  read_a(0, 0, af0);
-  // K step kt (stage kt & 1, record J of the block in registers).
-  auto step = [&](int kt, auto Jc) {
-    constexpr int J = decltype(Jc)::value;
-    read_a(kt & 1, 1, af1);
-    mfmas(wb, J, 0, af0);
-    __builtin_amdgcn_sched_barrier(0);
-    read_a(kt & 1, 2, af0);
-    mfmas(wb, J, 1, af1);
-    __builtin_amdgcn_sched_barrier(0);
-    read_a(kt & 1, 3, af1);
-    mfmas(wb, J, 2, af0);
-    __builtin_amdgcn_sched_barrier(0);
-    // Step kt+1's activations were copied at the previous barrier; at record 0 the copy of the next
-    // weight block (issued after them) may still be in flight.
-    if constexpr (J == 0) wait_vmem<NW>();
-    else wait_vmem<0>();
+  if constexpr (!BS) {
+    // Stepped schedule (128-row tiles: a K step's MFMAs are long enough to cover an activation copy).
+    // Prologue: weight block 0, activation steps 0 and 1; wait for block 0 and step 0 (step 1 may fly),
+    // read block 0 into registers and refill the buffer with block 1.
+    copy_w(kb0);
+    copy_a(kt0, 0);
+    copy_a(kt0 + 1, 1);
+    wait_vmem<MB>();
     __syncthreads();
-    copy_a(kt + 2, kt & 1);                  // every wave is done with this stage
-    read_a((kt + 1) & 1, 0, af0);
-    __builtin_amdgcn_sched_barrier(0);
-    mfmas(wb, J, 3, af1);
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr (J == 3) {                  // next block: complete since the wait above
-      read_block(wb, (kt >> 2) + 1);
-      wait_lds();
-      copy_w((kt >> 2) + 2);
+    read_block(wb, kb0);
+    wait_lds();
+    copy_w(kb0 + 1);
+    read_a(0, 0, af0);
+    // K step kt (stage kt & 1, record J of the block in registers).
+    auto step = [&](int kt, auto Jc) {
+      constexpr int J = decltype(Jc)::value;
+      read_a(kt & 1, 1, af1);
+      mfmas(wb, J, 0, af0);
+      __builtin_amdgcn_sched_barrier(0);
+      read_a(kt & 1, 2, af0);
+      mfmas(wb, J, 1, af1);
+      __builtin_amdgcn_sched_barrier(0);
+      read_a(kt & 1, 3, af1);
+      mfmas(wb, J, 2, af0);
+      __builtin_amdgcn_sched_barrier(0);
+      // Step kt+1's activations were copied at the previous barrier; at record 0 the copy of the next
+      // weight block (issued after them) may still be in flight.
+      if constexpr (J == 0) wait_vmem<NW>();
+      else wait_vmem<0>();
+      __syncthreads();
+      copy_a(kt + 2, kt & 1);                  // every wave is done with this stage
+      read_a((kt + 1) & 1, 0, af0);
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas(wb, J, 3, af1);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (J == 3) {                  // next block: complete since the wait above
+        read_block(wb, (kt >> 2) + 1);
+        wait_lds();
+        copy_w((kt >> 2) + 2);
+      }
+    };
+    for (int kt = kt0; kt < kt1; kt += 4) {     // kt0 is a multiple of 4: record J = kt % 4
+      step(kt, std::integral_constant<int, 0>{});
+      if (kt + 1 < kt1) step(kt + 1, std::integral_constant<int, 1>{});
+      if (kt + 2 < kt1) step(kt + 2, std::integral_constant<int, 2>{});
+      if (kt + 3 < kt1) step(kt + 3, std::integral_constant<int, 3>{});
     }
-  };
-  for (int kt = kt0; kt < kt1; kt += 4) {     // kt0 is a multiple of 4: record J = kt % 4
-    step(kt, std::integral_constant<int, 0>{});
-    if (kt + 1 < kt1) step(kt + 1, std::integral_constant<int, 1>{});
-    if (kt + 2 < kt1) step(kt + 2, std::integral_constant<int, 2>{});
-    if (kt + 3 < kt1) step(kt + 3, std::integral_constant<int, 3>{});
+  } else {
+    // Block schedule (narrow tiles, whose K steps are too short to cover a memory round trip): the
+    // activations of a whole 4-step block are copied together with its weights, into an 8-stage ring
+    // (stage kt & 7), so the copies of block b+1 fly during all four steps of block b and the wait and
+    // the barrier come once per block.
+    auto copy_a_blk = [&](int blk) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) copy_a(4 * blk + j, (4 * blk + j) & 7);
+    };
+    copy_w(kb0);
+    copy_a_blk(kb0);
+    wait_vmem<0>();
+    __syncthreads();
+    read_block(wb, kb0);
+    wait_lds();
+    if (kb0 + 1 < kb1) {
+      copy_w(kb0 + 1);
+      copy_a_blk(kb0 + 1);
+    }
+    read_a(kt0 & 7, 0, af0);
+    auto bstep = [&](int kt, auto Jc) {
+      constexpr int J = decltype(Jc)::value;
+      const int st = kt & 7;
+      read_a(st, 1, af1);
+      mfmas(wb, J, 0, af0);
+      __builtin_amdgcn_sched_barrier(0);
+      read_a(st, 2, af0);
+      mfmas(wb, J, 1, af1);
+      __builtin_amdgcn_sched_barrier(0);
+      read_a(st, 3, af1);
+      mfmas(wb, J, 2, af0);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (J < 3) read_a((kt + 1) & 7, 0, af0);   // same block: landed
+      mfmas(wb, J, 3, af1);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    for (int blk = kb0; blk < kb1; ++blk) {
+      const int kt = 4 * blk;
+      bstep(kt, std::integral_constant<int, 0>{});
+      if (kt + 1 < kt1) bstep(kt + 1, std::integral_constant<int, 1>{});
+      if (kt + 2 < kt1) bstep(kt + 2, std::integral_constant<int, 2>{});
+      if (kt + 3 < kt1) bstep(kt + 3, std::integral_constant<int, 3>{});
+      if (blk + 1 < kb1) {
+        wait_vmem<0>();                        // block blk+1's copies landed (this wave's) ...
+        __syncthreads();                       // ... and every wave's; all are done with block blk
+        read_block(wb, blk + 1);
+        wait_lds();
+        if (blk + 2 < kb1) {                   // block blk+2 reuses block blk's stages
+          copy_w(blk + 2);
+          copy_a_blk(blk + 2);
+        }
+        read_a((4 * blk + 4) & 7, 0, af0);
+      }
+    }
   }
   wait_vmem<0>();                            // the trailing (clamped) copies land before the LDS is released
 
-  if (part >= 0) {                           // raw partial tile [NM][128][128], finished by nv_splitk_finish
+  if (part >= 0) {                           // raw partial tile [NM][32 MB][128], finished by nv_splitk_finish
     float* pt = partials + (size_t)b * NM * PT;
     const int col = 32 * wave + li;
 #pragma unroll
@@ -640,8 +711,10 @@ __global__ void __launch_bounds__(256, 2) nv_gemm_kernel(int M, int K, int N, Nv
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          pt[t * PT + (32 * mb + 8 * (r >> 2) + 4 * h + (r & 3)) * 128 + col] = acc[t][mb][r];
+        for (int r = 0; r < 16; ++r) {
+          const int row = 32 * mb + 8 * (r >> 2) + 4 * h + (r & 3);
+          if (m0 + row < M) pt[t * PT + row * 128 + col] = acc[t][mb][r];   // the finish reads rows < M only
+        }
     return;
   }
 
@@ -700,7 +773,7 @@ __global__ void __launch_bounds__(256) nv_splitk_finish(int M, int N, NvPlan pla
   }
 }
 
-template <bool GU, int MB>
+template <bool GU, int MB, bool BS>
 hipError_t nv_launch(int M, int K, int N, const NvPlan& plan, const uint16_t* a16, const float* rowscale,
                      const uint8_t* w0, float inv0, const uint8_t* w1, float inv1, void* out, float* partials,
                      hipStream_t st) {
@@ -711,13 +784,13 @@ hipError_t nv_launch(int M, int K, int N, const NvPlan& plan, const uint16_t* a1
   if (e != hipSuccess) return e;
   const uint64_t bit = (uint64_t)1 << (dev & 63);
   if (!(raised.load() & bit)) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(nv_gemm_kernel<GU, MB>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, nv_lds_bytes(GU, MB));
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(nv_gemm_kernel<GU, MB, BS>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, nv_lds_bytes(GU, MB, BS));
     if (e != hipSuccess) return e;
     raised.fetch_or(bit);
   }
   const int grid = plan.units_grid + (plan.full + 7) / 8 * 8;
-  hipLaunchKernelGGL((nv_gemm_kernel<GU, MB>), dim3(grid), dim3(256), nv_lds_bytes(GU, MB), st, M, K, N, plan, a16,
+  hipLaunchKernelGGL((nv_gemm_kernel<GU, MB, BS>), dim3(grid), dim3(256), nv_lds_bytes(GU, MB, BS), st, M, K, N, plan, a16,
                      rowscale, w0, inv0, w1, inv1, out, partials);
   return hipGetLastError();
 }
@@ -729,9 +802,9 @@ hipError_t nv_dispatch(int M, int K, int N, const uint16_t* a16, const float* ro
   if (plan.units > 0 && partials == nullptr) return hipErrorInvalidValue;
   hipError_t e;
   switch (plan.bm) {
-    case 32: e = nv_launch<GU, 1>(M, K, N, plan, a16, rowscale, w0, inv0, w1, inv1, out, partials, st); break;
-    case 64: e = nv_launch<GU, 2>(M, K, N, plan, a16, rowscale, w0, inv0, w1, inv1, out, partials, st); break;
-    default: e = nv_launch<GU, 4>(M, K, N, plan, a16, rowscale, w0, inv0, w1, inv1, out, partials, st); break;
+    case 32: e = nv_launch<GU, 1, true>(M, K, N, plan, a16, rowscale, w0, inv0, w1, inv1, out, partials, st); break;
+    case 64: e = nv_launch<GU, 2, false>(M, K, N, plan, a16, rowscale, w0, inv0, w1, inv1, out, partials, st); break;
+    default: e = nv_launch<GU, 4, false>(M, K, N, plan, a16, rowscale, w0, inv0, w1, inv1, out, partials, st); break;
   }
   if (e != hipSuccess || plan.units == 0) return e;
   hipLaunchKernelGGL((nv_splitk_finish<GU>), dim3((plan.tiles - plan.full) * (plan.bm / 2)), dim3(256), 0, st, M, N,
