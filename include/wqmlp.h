@@ -84,7 +84,7 @@ int wq_last_hip_error(void);
  * Workspace (device bytes) that mlp_fp8w_run / mlp_nvfp4_run need for this
  * shape and path.  fmt: WQ_FMT_*; flags as for the run call.  Returns 0 for
  * invalid arguments or M == 0.
- *   GEMV path: act float32 [M, I].
+ *   GEMV path: act [M, I], float32 (FP8) or float16 (NVFP4).
  *   MFMA path: x as float16 [M, H] (row-scaled), per-row scales float32 [M],
  *              act float16 [M, I], then (NVFP4) float32 split-K partial
  *              tiles of at most 64 MiB; each region 256-byte aligned.
@@ -134,9 +134,11 @@ int mlp_fp8w_run(int64_t M, int64_t H, int64_t I, const void* x, int x_dtype,
  * scaled by its E4M3 group scale as it completes (GEMV) or the group scale is
  * folded exactly into the float16 decoded weight (MFMA); 1/global_scale
  * (rounded once to float32) multiplies the finished dot product.
- * MFMA path: x rows are scaled by a power of two and rounded to float16, and
- * act is rounded to float16 before the down GEMM; |act| must stay below
- * 65504 (larger values overflow to inf and propagate into out).
+ * act = silu(g) * u is rounded to float16 before the down projection on both
+ * paths (the page's own kernels quantize activations more coarsely); |act|
+ * must stay below 65504 (larger values overflow to inf and propagate into
+ * out).  MFMA path: x rows are also scaled by a power of two and rounded to
+ * float16.  GEMV path: bitwise M-independent as for mlp_fp8w_run.
  */
 int mlp_nvfp4_run(int64_t M, int64_t H, int64_t I, const void* x, int x_dtype,
                   const uint8_t* gate_blk, float gate_global_scale,

@@ -140,10 +140,14 @@ size_t mlp_partials(int fmt, int64_t M, int64_t H, int64_t I) {
                   wq::mfma_partial_bytes(f, (int)M, (int)I, (int)H, false));
 }
 
+// GEMV path act element: float32 for FP8 (no rounding between the GEMMs, as the FP8 definition asks),
+// float16 for NVFP4.
+size_t act_gemv_bytes(int fmt) { return fmt == WQ_FMT_NVFP4 ? 2 : 4; }
+
 // Workspace of the two-layer MLP; 0 means "invalid".
 size_t mlp_ws(int fmt, int64_t M, int64_t H, int64_t I, int flags) {
   if (M <= 0 || H <= 0 || I <= 0 || M > kMaxDim || H > kMaxDim || I > kMaxDim) return 0;
-  if (mlp_path(fmt, M, H, I, flags) == WQ_PATH_GEMV) return align256((size_t)M * I * 4);
+  if (mlp_path(fmt, M, H, I, flags) == WQ_PATH_GEMV) return align256((size_t)M * I * act_gemv_bytes(fmt));
   return align256((size_t)M * H * 2) + align256((size_t)M * 4) + align256((size_t)M * I * 2) +
          align256(mlp_partials(fmt, M, H, I));
 }
@@ -155,7 +159,8 @@ bool shape_ok(int fmt, int path, int64_t H, int64_t I, int x_dtype) {
   } else if (H % 16 || I % 16) {
     return false;
   }
-  if (path == WQ_PATH_GEMV && (!gemv_fits(fmt, H, x_dtype) || !gemv_fits(fmt, I, WQ_F32))) return false;
+  if (path == WQ_PATH_GEMV && (!gemv_fits(fmt, H, x_dtype) || !gemv_fits(fmt, I, fmt == WQ_FMT_NVFP4 ? WQ_F16 : WQ_F32)))
+    return false;
   return true;
 }
 
@@ -195,15 +200,15 @@ int mlp_run(int fmt, int64_t M, int64_t H, int64_t I, const void* x, int x_dtype
   const wq::XType xt = x_dtype == WQ_BF16 ? wq::X_BF16 : wq::X_F32;
   const int m = (int)M, h = (int)H, i = (int)I;
   if (path == WQ_PATH_GEMV) {
-    float* act = reinterpret_cast<float*>(ws);
+    float* act = reinterpret_cast<float*>(ws);          // FP8: float32; NVFP4: float16 bits
     if (fmt == WQ_FMT_FP8W) {
       if (do_gu) rc = launched(wq::launch_fp8w_gemv(m, h, i, x, xt, wg, sg, wu, su, act, st));
       if (rc == WQ_OK && do_down)
         rc = launched(wq::launch_fp8w_gemv(m, i, h, act, wq::X_F32, wd, sd, nullptr, nullptr, out, st));
     } else {
-      if (do_gu) rc = launched(wq::launch_nvfp4_gemv(m, h, i, x, xt, wg, 1.0f / gg, wu, 1.0f / gu, act, st));
+      if (do_gu) rc = launched(wq::launch_nvfp4_gemv(m, h, i, x, xt, wg, 1.0f / gg, wu, 1.0f / gu, act, true, st));
       if (rc == WQ_OK && do_down)
-        rc = launched(wq::launch_nvfp4_gemv(m, i, h, act, wq::X_F32, wd, 1.0f / gd, nullptr, 0.f, out, st));
+        rc = launched(wq::launch_nvfp4_gemv(m, i, h, act, wq::X_F16, wd, 1.0f / gd, nullptr, 0.f, out, false, st));
     }
     return rc;
   }
@@ -400,7 +405,7 @@ int qlinear_run(int fmt, int64_t M, int64_t N, int64_t K, const void* x, int x_d
   if (path == WQ_PATH_GEMV) {
     if (fmt == WQ_FMT_FP8W)
       return launched(wq::launch_fp8w_gemv((int)M, (int)K, (int)N, x, xt, w, scale, nullptr, nullptr, y, st));
-    return launched(wq::launch_nvfp4_gemv((int)M, (int)K, (int)N, x, xt, w, inv, nullptr, 0.f, y, st));
+    return launched(wq::launch_nvfp4_gemv((int)M, (int)K, (int)N, x, xt, w, inv, nullptr, 0.f, y, false, st));
   }
   uint8_t* base = reinterpret_cast<uint8_t*>(workspace);
   uint16_t* x16 = reinterpret_cast<uint16_t*>(base);

@@ -73,6 +73,26 @@ __device__ __forceinline__ float dot2_f16(f16x2 a, f16x2 b, float acc) {
   return __builtin_amdgcn_fdot2(a, b, acc, false);
 }
 
+// ---- global->LDS copies ------------------------------------------------------------------------
+// Copy 16 bytes per lane from sbase + voff into LDS at lds_base + 16 * lane (lds_base wave-uniform).
+// M0 carries the LDS address; nothing else in the kernels that use it needs M0, so clobbering it is safe
+// (the compiler warns about clobbering a reserved register in general).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_copy16(uint32_t voff, const void* sbase, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds_base)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+// s_waitcnt vmcnt(N) with the other counters left alone (the copies above are invisible to the compiler's
+// own counter tracking, so every wait on them is explicit).
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }   // lgkmcnt(0)
+
 // ---- reductions -----------------------------------------------------------------------------
 // Butterfly sum over groups of W lanes (W = 16 or 64): xor offsets W/2, ..., 1.
 // The order is fixed, so the result is bitwise reproducible and equal in all lanes.

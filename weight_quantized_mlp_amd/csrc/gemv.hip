@@ -202,12 +202,14 @@ __global__ void __launch_bounds__(256) fp8w_gemv_kernel(int M, int K, int N, int
 }
 
 // ===================================== NVFP4 Block64 ===========================================
-template <typename XT, bool GU, int MR, int SEG>
+// XF16 (16-bit XT only): x holds float16 bits, else bfloat16 bits.  Y16: y is stored as float16 bits
+// (the NVFP4 MLP's act), else float32.
+template <typename XT, bool GU, int MR, int SEG, bool XF16, bool Y16>
 __global__ void __launch_bounds__(256) nvfp4_gemv_kernel(int M, int K, int N, int rpw,
                                                         const XT* __restrict__ x,
                                                         const uint8_t* __restrict__ b0, float inv0,
                                                         const uint8_t* __restrict__ b1, float inv1,
-                                                        float* __restrict__ y) {
+                                                        void* __restrict__ y) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   constexpr int NM = GU ? 2 : 1;
   constexpr int STRIDE = 64 * (int)sizeof(XT) + 16;
@@ -285,6 +287,16 @@ __global__ void __launch_bounds__(256) nvfp4_gemv_kernel(int M, int K, int N, in
                     const u32x4 x0 = *reinterpret_cast<const u32x4*>(xl + 32 * g);
                     const u32x4 x1 = *reinterpret_cast<const u32x4*>(xl + 32 * g + 16);
                     const uint32_t w0 = qs[2 * g], w1 = qs[2 * g + 1];
+                    if constexpr (XF16) {
+                      part = dot2_f16(e2m1x2_f16<0>(w0), as_f16x2(x0.x), part);
+                      part = dot2_f16(e2m1x2_f16<1>(w0), as_f16x2(x0.y), part);
+                      part = dot2_f16(e2m1x2_f16<2>(w0), as_f16x2(x0.z), part);
+                      part = dot2_f16(e2m1x2_f16<3>(w0), as_f16x2(x0.w), part);
+                      part = dot2_f16(e2m1x2_f16<0>(w1), as_f16x2(x1.x), part);
+                      part = dot2_f16(e2m1x2_f16<1>(w1), as_f16x2(x1.y), part);
+                      part = dot2_f16(e2m1x2_f16<2>(w1), as_f16x2(x1.z), part);
+                      part = dot2_f16(e2m1x2_f16<3>(w1), as_f16x2(x1.w), part);
+                    } else {
                     part = dot2_bf16(e2m1x2_bf16<0>(w0), x0.x, part);
                     part = dot2_bf16(e2m1x2_bf16<1>(w0), x0.y, part);
                     part = dot2_bf16(e2m1x2_bf16<2>(w0), x0.z, part);
@@ -293,6 +305,7 @@ __global__ void __launch_bounds__(256) nvfp4_gemv_kernel(int M, int K, int N, in
                     part = dot2_bf16(e2m1x2_bf16<1>(w1), x1.y, part);
                     part = dot2_bf16(e2m1x2_bf16<2>(w1), x1.z, part);
                     part = dot2_bf16(e2m1x2_bf16<3>(w1), x1.w, part);
+                    }
                   } else {
 #pragma unroll
                     for (int h = 0; h < 2; ++h) {
@@ -344,7 +357,8 @@ __global__ void __launch_bounds__(256) nvfp4_gemv_kernel(int M, int K, int N, in
             } else {
               r = v[0] * inv0;
             }
-            y[(size_t)m * N + row] = r;
+            if constexpr (Y16) reinterpret_cast<uint16_t*>(y)[(size_t)m * N + row] = __builtin_bit_cast(uint16_t, (_Float16)r);
+            else reinterpret_cast<float*>(y)[(size_t)m * N + row] = r;
           }
         }
       }
@@ -423,9 +437,9 @@ hipError_t fp8_dispatch(int M, int K, int N, const void* x, const uint8_t* w0, c
   return hipGetLastError();
 }
 
-template <typename XT, bool GU>
+template <typename XT, bool GU, bool XF16, bool Y16>
 hipError_t nvfp4_dispatch(int M, int K, int N, const void* x, const uint8_t* b0, float inv0,
-                          const uint8_t* b1, float inv1, float* y, hipStream_t st) {
+                          const uint8_t* b1, float inv1, void* y, hipStream_t st) {
   constexpr int STRIDE = 64 * (int)sizeof(XT) + 16;
   const size_t per_row = (size_t)(K / 64) * STRIDE;
   const bool slab4 = M > 1 && 4 * per_row <= kLdsBudget;
@@ -433,12 +447,12 @@ hipError_t nvfp4_dispatch(int M, int K, int N, const void* x, const uint8_t* b0,
   const Shape sh = pick_shape(N, lds, 4);
   constexpr int SEG = GU ? 1 : 2;
   if (slab4) {
-    auto kern = nvfp4_gemv_kernel<XT, GU, 4, SEG>;
+    auto kern = nvfp4_gemv_kernel<XT, GU, 4, SEG, XF16, Y16>;
     set_lds_limit(kern, lds);
     hipLaunchKernelGGL(kern, dim3(sh.grid), dim3(sh.threads), lds, st, M, K, N, sh.rpw,
                        reinterpret_cast<const XT*>(x), b0, inv0, b1, inv1, y);
   } else {
-    auto kern = nvfp4_gemv_kernel<XT, GU, 1, SEG>;
+    auto kern = nvfp4_gemv_kernel<XT, GU, 1, SEG, XF16, Y16>;
     set_lds_limit(kern, lds);
     hipLaunchKernelGGL(kern, dim3(sh.grid), dim3(sh.threads), lds, st, M, K, N, sh.rpw,
                        reinterpret_cast<const XT*>(x), b0, inv0, b1, inv1, y);
@@ -460,14 +474,21 @@ hipError_t launch_fp8w_gemv(int M, int K, int N, const void* x, XType xt, const 
 }
 
 hipError_t launch_nvfp4_gemv(int M, int K, int N, const void* x, XType xt, const uint8_t* b0, float inv0,
-                             const uint8_t* b1, float inv1, float* y, hipStream_t st) {
+                             const uint8_t* b1, float inv1, void* y, bool y16, hipStream_t st) {
   const bool gu = b1 != nullptr;
-  if (fast_gemv_nvfp4_ok(K, xt, gu)) return launch_fast_nvfp4(M, K, N, x, xt, b0, inv0, b1, inv1, y, st);
-  if (xt == X_BF16)
-    return gu ? nvfp4_dispatch<uint16_t, true>(M, K, N, x, b0, inv0, b1, inv1, y, st)
-              : nvfp4_dispatch<uint16_t, false>(M, K, N, x, b0, inv0, b1, inv1, y, st);
-  return gu ? nvfp4_dispatch<float, true>(M, K, N, x, b0, inv0, b1, inv1, y, st)
-            : nvfp4_dispatch<float, false>(M, K, N, x, b0, inv0, b1, inv1, y, st);
+  if (y16 && !gu) return hipErrorInvalidValue;
+  if (fast_gemv_nvfp4_ok(K, xt, gu)) return launch_fast_nvfp4(M, K, N, x, xt, b0, inv0, b1, inv1, y, y16, st);
+  if (gu) {
+    if (xt == X_BF16)
+      return y16 ? nvfp4_dispatch<uint16_t, true, false, true>(M, K, N, x, b0, inv0, b1, inv1, y, st)
+                 : nvfp4_dispatch<uint16_t, true, false, false>(M, K, N, x, b0, inv0, b1, inv1, y, st);
+    if (xt == X_F16) return hipErrorInvalidValue;
+    return y16 ? nvfp4_dispatch<float, true, false, true>(M, K, N, x, b0, inv0, b1, inv1, y, st)
+               : nvfp4_dispatch<float, true, false, false>(M, K, N, x, b0, inv0, b1, inv1, y, st);
+  }
+  if (xt == X_BF16) return nvfp4_dispatch<uint16_t, false, false, false>(M, K, N, x, b0, inv0, b1, inv1, y, st);
+  if (xt == X_F16) return nvfp4_dispatch<uint16_t, false, true, false>(M, K, N, x, b0, inv0, b1, inv1, y, st);
+  return nvfp4_dispatch<float, false, false, false>(M, K, N, x, b0, inv0, b1, inv1, y, st);
 }
 
 }  // namespace wq

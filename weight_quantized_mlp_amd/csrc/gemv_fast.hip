@@ -16,6 +16,9 @@
 //    lane -- are dealt round-robin to the waves, each wave streaming its items with the next D loads in
 //    flight; each wave keeps one partial per row it touches and the workgroup adds the 16 partials of a
 //    row in wave order.
+//  * nv_lin_r32 (NVFP4 single linear with 16-bit activations, K % 256 == 0; the NVFP4 MLP's down
+//    projection, whose act is float16): single-row items of 32 records moved by global->LDS copies,
+//    rows interleaved over the grid (described at the kernel).
 // The per-lane unit is 16 weights for both formats: an FP8 chunk (16 code bytes) or an NVFP4 group (the
 // 8 nibble bytes qs[8q..8q+7] of a Block64 record and its scale byte d[q]).  Four lanes read one record,
 // so the 36-byte records are covered without gaps and K = 5120 fills every lane (320 groups per row).
@@ -189,11 +192,12 @@ __global__ void __launch_bounds__(64 * kRowWaves) fp8_gu_row(int M, int K, int N
 // record's scale byte d[q].  Lane l owns groups l, l+64, ... of its row; the four lanes 4j..4j+3 read
 // record j's 32 nibble bytes contiguously, so a wave's loads cover the row's records without gaps.
 // Workgroup shape and x staging as in the FP8 row kernel.
-template <int CH, bool ONE>
+// O16: act is stored as float16 bits (the NVFP4 MLP's act), else float32.
+template <int CH, bool ONE, bool O16>
 __global__ void __launch_bounds__(64 * kRowWaves) nv_gu_grp(int M, int K, int N, const uint16_t* __restrict__ x,
                                                          const uint8_t* __restrict__ bg, float inv_g,
                                                          const uint8_t* __restrict__ bu, float inv_u,
-                                                         float* __restrict__ act) {
+                                                         void* __restrict__ act) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int G = K >> 4;
   const size_t rb = (size_t)(K >> 6) * 36;
@@ -251,9 +255,38 @@ __global__ void __launch_bounds__(64 * kRowWaves) nv_gu_grp(int M, int K, int N,
     if (row < N) {
       const float gv = gsum<64>(acc[0]) * inv_g;
       const float uv = gsum<64>(acc[1]) * inv_u;
-      if (lane == 0) act[(size_t)m * N + row] = silu_f32(gv) * uv;
+      const float a = silu_f32(gv) * uv;
+      if (lane == 0) {
+        if constexpr (O16) reinterpret_cast<uint16_t*>(act)[(size_t)m * N + row] = __builtin_bit_cast(uint16_t, (_Float16)a);
+        else reinterpret_cast<float*>(act)[(size_t)m * N + row] = a;
+      }
     }
   }
+}
+
+// Sum over one 16-weight group of E2M1 weight x float16 activation, float32 accumulation in ascending k:
+// w0, w1 hold the group's 8 nibble bytes (low nibble first), x0, x1 its 16 activations (f16 pairs).
+__device__ __forceinline__ float dot16_e2m1_f16(uint32_t w0, uint32_t w1, u32x4 x0, u32x4 x1, float acc) {
+  acc = dot2_f16(e2m1x2_f16<0>(w0), as_f16x2(x0.x), acc);
+  acc = dot2_f16(e2m1x2_f16<1>(w0), as_f16x2(x0.y), acc);
+  acc = dot2_f16(e2m1x2_f16<2>(w0), as_f16x2(x0.z), acc);
+  acc = dot2_f16(e2m1x2_f16<3>(w0), as_f16x2(x0.w), acc);
+  acc = dot2_f16(e2m1x2_f16<0>(w1), as_f16x2(x1.x), acc);
+  acc = dot2_f16(e2m1x2_f16<1>(w1), as_f16x2(x1.y), acc);
+  acc = dot2_f16(e2m1x2_f16<2>(w1), as_f16x2(x1.z), acc);
+  acc = dot2_f16(e2m1x2_f16<3>(w1), as_f16x2(x1.w), acc);
+  return acc;
+}
+__device__ __forceinline__ float dot16_e2m1_bf16(uint32_t w0, uint32_t w1, u32x4 x0, u32x4 x1, float acc) {
+  acc = dot2_bf16(e2m1x2_bf16<0>(w0), x0.x, acc);
+  acc = dot2_bf16(e2m1x2_bf16<1>(w0), x0.y, acc);
+  acc = dot2_bf16(e2m1x2_bf16<2>(w0), x0.z, acc);
+  acc = dot2_bf16(e2m1x2_bf16<3>(w0), x0.w, acc);
+  acc = dot2_bf16(e2m1x2_bf16<0>(w1), x1.x, acc);
+  acc = dot2_bf16(e2m1x2_bf16<1>(w1), x1.y, acc);
+  acc = dot2_bf16(e2m1x2_bf16<2>(w1), x1.z, acc);
+  acc = dot2_bf16(e2m1x2_bf16<3>(w1), x1.w, acc);
+  return acc;
 }
 
 // ---- item kernels ---------------------------------------------------------------------------------
@@ -406,7 +439,8 @@ __global__ void __launch_bounds__(64 * kItemWaves, 8) fp8_lin_items(int M, int K
 
 // NVFP4 single linear: y[m, n] = inv * sum_k xa[m, k] dq(blk[n, k]).  Same item schedule as the FP8
 // kernel, with the 16-weight group (8 nibble bytes + its scale byte) as the per-lane unit.
-template <typename XT, bool ONE>
+// F16 (16-bit XT only): x holds float16 bits, else bfloat16 bits.
+template <typename XT, bool ONE, bool F16>
 __global__ void __launch_bounds__(64 * kItemWaves, 8) nv_lin_grp(int M, int K, int N, const XT* __restrict__ xa,
                                                               const uint8_t* __restrict__ blk, float inv,
                                                               float* __restrict__ y) {
@@ -520,6 +554,11 @@ __global__ void __launch_bounds__(64 * kItemWaves, 8) nv_lin_grp(int M, int K, i
               for (int r = 0; r < R; ++r) {
                 const u32x2 w = qb[b][r];
                 float pt = 0.f;
+                if constexpr (F16) {
+                  pt = dot16_e2m1_f16(w.x, w.y, x0, x1, pt);
+                  acc[r] = fmaf(pt, e4m3_byte_f32<0>(sb[b][r]), acc[r]);
+                  continue;
+                }
                 pt = dot2_bf16(e2m1x2_bf16<0>(w.x), x0.x, pt);
                 pt = dot2_bf16(e2m1x2_bf16<1>(w.x), x0.y, pt);
                 pt = dot2_bf16(e2m1x2_bf16<2>(w.x), x0.z, pt);
@@ -540,6 +579,130 @@ __global__ void __launch_bounds__(64 * kItemWaves, 8) nv_lin_grp(int M, int K, i
     __syncthreads();
     if (threadIdx.x < RB) {
       const int n = rbase + threadIdx.x;
+      if (n < N) {
+        float v = 0.f;
+        for (int ww = 0; ww < NW; ++ww) v += part[ww][threadIdx.x];
+        y[(size_t)m * N + n] = v * inv;
+      }
+    }
+  }
+}
+
+// NVFP4 single linear for 16-bit activations, K % 256 == 0: y[m, n] = inv * sum_k xa[m, k] dq(blk[n, k]).
+// A 16-wave workgroup owns kR32Rows output rows, interleaved over the grid (local row i is row
+// blockIdx + gridDim * i), so the rows the chip streams at any moment sit in two narrow windows of the
+// matrix.  Work item (row i, slot t) = the 32 records [32 t, 32 t + 32) of the row, 1152 contiguous
+// bytes; items are dealt round-robin to the waves.  Both the activation row and the items move by
+// global->LDS copies (kR32Depth items in flight per wave, explicit vmcnt waits): register loads of
+// the same data made the compiler wait for every outstanding load at the top of the item loop.
+// Lane l of an item owns groups 2l, 2l+1 (record l / 2, 16 nibble bytes and 2 scale bytes).
+// Accumulation order (fixed; M-independent): per lane, group 2l then 2l+1, each a 16-weight partial in
+// ascending k times its E4M3 scale; per wave and row, items ascending, a 64-lane sum (wave64_sum) when
+// the wave leaves the row; per row, the 16 wave partials in wave order; times inv.
+constexpr int kR32Rows = 20, kR32Depth = 2, kR32Item = 1152;
+constexpr size_t r32_lds_bytes(int K) { return (size_t)K * 2 + (size_t)kItemWaves * kR32Depth * kR32Item; }
+
+template <bool F16, bool ONE>
+__global__ void __launch_bounds__(64 * kItemWaves) nv_lin_r32(int M, int K, int N, const uint16_t* __restrict__ xa,
+                                                           const uint8_t* __restrict__ blk, float inv,
+                                                           float* __restrict__ y) {
+  constexpr int NW = kItemWaves, RB = kR32Rows, D = kR32Depth;
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  __shared__ float part[NW][RB];
+  const int U = K >> 5;                                // two-group units per row
+  const int T = (U + 63) >> 6;                         // 32-record slots per row
+  const uint32_t rb = (uint32_t)(K >> 6) * 36u;        // a multiple of 16
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int NI = RB * T;
+  const int nk = NI > wv ? (NI - wv + NW - 1) / NW : 0;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
+  const uint32_t abytes = (uint32_t)K * 2u;
+  const uint32_t ring = lds0 + abytes + (uint32_t)wv * D * kR32Item;
+  const uint8_t* ringp = lds + abytes + wv * D * kR32Item;
+  auto rowof = [&](int i) { return (int)blockIdx.x + (int)gridDim.x * i; };
+  // copies of an item: chunk c < 72 at 1152 t + 16 c of the row; chunks past the row's end (last slot)
+  // are clamped to its last chunk: in bounds, and they belong to units >= U, never used
+  const uint32_t q0 = 16u * lane, q1 = 16u * (64 + (lane & 7));
+  // the lane's unit inside an item: nibbles at 36 (l / 2) + 4 + 16 (l % 2), scale bytes at 36 (l / 2) + 2 (l % 2)
+  const uint32_t qoff = (uint32_t)(lane >> 1) * 36u + 4u + 16u * (lane & 1);
+  const uint32_t soff = (uint32_t)(lane >> 1) * 36u + 2u * (lane & 1);
+  const int nslot = U * 4;                             // 16-byte activation pieces per row
+  const int Mloop = ONE ? 1 : M;
+  for (int m = 0; m < Mloop; ++m) {
+    if (m) __syncthreads();                            // the previous row's LDS reads are done
+    for (int i = threadIdx.x; i < NW * RB; i += blockDim.x) (&part[0][0])[i] = 0.f;
+    // activation row m, piece-major: LDS slot s = q U + u holds piece 4 u + q of the row
+    const uint16_t* xm = xa + (size_t)m * K;
+    for (int j = 0; 64 * (wv + NW * j) < nslot; ++j) {
+      const int sl = 64 * (wv + NW * j) + lane;
+      if (sl < nslot) {
+        const int q = sl / U, u = sl - q * U;
+        lds_copy16((uint32_t)(4 * u + q) * 16u, xm, __builtin_amdgcn_readfirstlane(lds0 + 1024u * (wv + NW * j)));
+      }
+    }
+    int lg = wv / T, lt = wv - (wv / T) * T, lk = 0;
+    auto issue = [&](int stage) {
+      const uint32_t st = ring + stage * kR32Item;
+      const uint32_t base = (uint32_t)min(rowof(lg), N - 1) * rb, off = 1152u * lt;
+      lds_copy16(base + min(off + q0, rb - 16u), blk, __builtin_amdgcn_readfirstlane(st));
+      if (lane < 8) lds_copy16(base + min(off + q1, rb - 16u), blk, __builtin_amdgcn_readfirstlane(st + 1024));
+      ++lk;
+      if (lk < nk) {                                   // past the wave's last item: repeat it (never used)
+        lt += NW;
+        while (lt >= T) { lt -= T; ++lg; }
+      }
+    };
+#pragma unroll
+    for (int d = 0; d < D; ++d) issue(d);
+    wait_vmem<2 * D>();                                // this wave's activation copies landed ...
+    __syncthreads();                                   // ... and every wave's
+    float acc = 0.f;
+    int cur = -1;
+    auto flush = [&]() {
+      if (cur < 0) return;
+      const float v = wave64_sum(acc);
+      acc = 0.f;
+      if (lane == 0) part[wv][cur] = v;
+    };
+    int cg = wv / T, ct = wv - (wv / T) * T;
+    for (int k = 0; k < nk; ++k) {
+      const int stage = k & (D - 1);
+      wait_vmem<2 * (D - 1)>();                        // item k's two copies landed
+      const int gi = cg, u = lane + 64 * ct;
+      ct += NW;
+      while (ct >= T) { ct -= T; ++cg; }
+      if (gi != cur) {
+        flush();
+        cur = gi;
+      }
+      if (u < U) {
+        const uint8_t* sp = ringp + stage * kR32Item;
+        const uint32_t* wp = reinterpret_cast<const uint32_t*>(sp + qoff);
+        const uint32_t w0 = wp[0], w1 = wp[1], w2 = wp[2], w3 = wp[3];
+        const uint32_t sc = *reinterpret_cast<const uint16_t*>(sp + soff);
+        u32x4 xv[4];
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) xv[qq] = *reinterpret_cast<const u32x4*>(lds + ((size_t)qq * U + u) * 16);
+        float p0, p1;
+        if constexpr (F16) {
+          p0 = dot16_e2m1_f16(w0, w1, xv[0], xv[1], 0.f);
+          p1 = dot16_e2m1_f16(w2, w3, xv[2], xv[3], 0.f);
+        } else {
+          p0 = dot16_e2m1_bf16(w0, w1, xv[0], xv[1], 0.f);
+          p1 = dot16_e2m1_bf16(w2, w3, xv[2], xv[3], 0.f);
+        }
+        acc = fmaf(p0, e4m3_byte_f32<0>(sc), acc);
+        acc = fmaf(p1, e4m3_byte_f32<1>(sc), acc);
+      }
+      wait_lds();                                      // the stage's LDS reads are done before its refill
+      issue(stage);                                    // item k + D
+    }
+    flush();
+    wait_vmem<0>();                                    // trailing copies land before the LDS is reused
+    __syncthreads();
+    if (threadIdx.x < RB) {
+      const int n = rowof(threadIdx.x);
       if (n < N) {
         float v = 0.f;
         for (int ww = 0; ww < NW; ++ww) v += part[ww][threadIdx.x];
@@ -570,6 +733,7 @@ bool fast_gemv_fp8_ok(int K, XType xt, bool gu) {
 bool fast_gemv_nvfp4_ok(int K, XType xt, bool gu) {
   if (K % 64) return false;
   if (gu) return xt == X_BF16 && (K / 16 + 63) / 64 <= 8;
+  if (xt != X_F32 && K % 256 == 0 && r32_lds_bytes(K) <= kMaxItemLds) return true;
   return (size_t)K * (xt == X_F32 ? 4 : 2) <= kMaxItemLds;
 }
 
@@ -611,7 +775,7 @@ hipError_t launch_fast_fp8(int M, int K, int N, const void* x, XType xt, const u
 }
 
 hipError_t launch_fast_nvfp4(int M, int K, int N, const void* x, XType xt, const uint8_t* b0, float inv0,
-                             const uint8_t* b1, float inv1, float* y, hipStream_t st) {
+                             const uint8_t* b1, float inv1, void* y, bool y16, hipStream_t st) {
   if (b1 != nullptr) {
     const int CH = (K / 16 + 63) / 64;
     const dim3 grid((N + kRowWaves - 1) / kRowWaves), block(64 * kRowWaves);
@@ -620,8 +784,10 @@ hipError_t launch_fast_nvfp4(int M, int K, int N, const void* x, XType xt, const
     switch (CH) {
 #define WQ_CASE(n)                                                                                           \
   case n:                                                                                                    \
-    if (M == 1) hipLaunchKernelGGL((nv_gu_grp<n, true>), grid, block, lds, st, M, K, N, xb, b0, inv0, b1, inv1, y); \
-    else hipLaunchKernelGGL((nv_gu_grp<n, false>), grid, block, lds, st, M, K, N, xb, b0, inv0, b1, inv1, y);      \
+    if (M == 1 && y16) hipLaunchKernelGGL((nv_gu_grp<n, true, true>), grid, block, lds, st, M, K, N, xb, b0, inv0, b1, inv1, y);  \
+    else if (M == 1) hipLaunchKernelGGL((nv_gu_grp<n, true, false>), grid, block, lds, st, M, K, N, xb, b0, inv0, b1, inv1, y); \
+    else if (y16) hipLaunchKernelGGL((nv_gu_grp<n, false, true>), grid, block, lds, st, M, K, N, xb, b0, inv0, b1, inv1, y);   \
+    else hipLaunchKernelGGL((nv_gu_grp<n, false, false>), grid, block, lds, st, M, K, N, xb, b0, inv0, b1, inv1, y);           \
     break;
       WQ_CASE(1) WQ_CASE(2) WQ_CASE(3) WQ_CASE(4) WQ_CASE(5) WQ_CASE(6) WQ_CASE(7) WQ_CASE(8)
 #undef WQ_CASE
@@ -629,19 +795,43 @@ hipError_t launch_fast_nvfp4(int M, int K, int N, const void* x, XType xt, const
     }
     return hipGetLastError();
   }
+  if (y16) return hipErrorInvalidValue;                // a single linear writes float32
+  float* yf = reinterpret_cast<float*>(y);
+  if (xt != X_F32 && K % 256 == 0 && r32_lds_bytes(K) <= kMaxItemLds) {
+    const size_t lds = r32_lds_bytes(K);
+    const dim3 grid((N + kR32Rows - 1) / kR32Rows), block(64 * kItemWaves);
+    const uint16_t* xb = reinterpret_cast<const uint16_t*>(x);
+#define WQ_LAUNCH(F, O)                                                                                      \
+  do {                                                                                                       \
+    if (!lds_ok(nv_lin_r32<F, O>, lds)) return hipErrorInvalidValue;                                         \
+    hipLaunchKernelGGL((nv_lin_r32<F, O>), grid, block, lds, st, M, K, N, xb, b0, inv0, yf);                 \
+  } while (0)
+    if (xt == X_F16) {
+      if (M == 1) WQ_LAUNCH(true, true);
+      else WQ_LAUNCH(true, false);
+    } else {
+      if (M == 1) WQ_LAUNCH(false, true);
+      else WQ_LAUNCH(false, false);
+    }
+#undef WQ_LAUNCH
+    return hipGetLastError();
+  }
   const size_t lds = (size_t)K * (xt == X_F32 ? 4 : 2);
   const dim3 grid((N + kItemRows - 1) / kItemRows), block(64 * kItemWaves);
-#define WQ_LAUNCH(T, O)                                                                                      \
+#define WQ_LAUNCH(T, O, F)                                                                                   \
   do {                                                                                                       \
-    if (!lds_ok(nv_lin_grp<T, O>, lds)) return hipErrorInvalidValue;                                       \
-    hipLaunchKernelGGL((nv_lin_grp<T, O>), grid, block, lds, st, M, K, N, reinterpret_cast<const T*>(x), b0, inv0, y); \
+    if (!lds_ok(nv_lin_grp<T, O, F>, lds)) return hipErrorInvalidValue;                                      \
+    hipLaunchKernelGGL((nv_lin_grp<T, O, F>), grid, block, lds, st, M, K, N, reinterpret_cast<const T*>(x), b0, inv0, yf); \
   } while (0)
   if (xt == X_F32) {
-    if (M == 1) WQ_LAUNCH(float, true);
-    else WQ_LAUNCH(float, false);
+    if (M == 1) WQ_LAUNCH(float, true, false);
+    else WQ_LAUNCH(float, false, false);
+  } else if (xt == X_F16) {
+    if (M == 1) WQ_LAUNCH(uint16_t, true, true);
+    else WQ_LAUNCH(uint16_t, false, true);
   } else {
-    if (M == 1) WQ_LAUNCH(uint16_t, true);
-    else WQ_LAUNCH(uint16_t, false);
+    if (M == 1) WQ_LAUNCH(uint16_t, true, false);
+    else WQ_LAUNCH(uint16_t, false, false);
   }
 #undef WQ_LAUNCH
   return hipGetLastError();

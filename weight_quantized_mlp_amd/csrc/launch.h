@@ -16,10 +16,12 @@ enum XType { X_F32 = 0, X_BF16 = 1, X_F16 = 2 };
 hipError_t launch_fp8w_gemv(int M, int K, int N, const void* x, XType xt,
                             const uint8_t* w0, const float* s0, const uint8_t* w1, const float* s1,
                             float* y, hipStream_t st);
-// NVFP4 Block64: same with the per-tensor factors inv0 = 1/gs0, inv1 = 1/gs1.
+// NVFP4 Block64: same with the per-tensor factors inv0 = 1/gs0, inv1 = 1/gs1.  x: X_F32, X_BF16, or
+// (single matrix only) X_F16.  y16 (gate+up only): y is float16 [M, N] (the NVFP4 MLP's act), else
+// float32.
 hipError_t launch_nvfp4_gemv(int M, int K, int N, const void* x, XType xt,
                              const uint8_t* b0, float inv0, const uint8_t* b1, float inv1,
-                             float* y, hipStream_t st);
+                             void* y, bool y16, hipStream_t st);
 
 // Main M < 128 kernels (gemv_fast.hip); the *_ok predicates say whether a shape is covered.
 // For a given shape the same family serves every M < 128, so row results do not depend on M.
@@ -28,7 +30,7 @@ bool fast_gemv_nvfp4_ok(int K, XType xt, bool gu);
 hipError_t launch_fast_fp8(int M, int K, int N, const void* x, XType xt, const uint8_t* w0, const float* s0,
                            const uint8_t* w1, const float* s1, float* y, hipStream_t st);
 hipError_t launch_fast_nvfp4(int M, int K, int N, const void* x, XType xt, const uint8_t* b0, float inv0,
-                             const uint8_t* b1, float inv1, float* y, hipStream_t st);
+                             const uint8_t* b1, float inv1, void* y, bool y16, hipStream_t st);
 
 // ---- M >= 128: MFMA GEMM family ---------------------------------------------------------------
 // x [M,K] (f32 or bf16) -> x16 [M,K] f16 scaled per row by 2^-e, rowscale[m] = 2^e.
