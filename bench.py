@@ -54,6 +54,8 @@ def parse():
                     help="only run this many plain (non-graph) headline steps, for rocprofv3 --pmc passes")
     ap.add_argument("--prefill-counters", type=int, default=0,
                     help="only run this many plain NVFP4 M=512 prefill steps, for rocprofv3 --pmc passes")
+    ap.add_argument("--decode-counters", type=int, default=0,
+                    help="only run this many plain NVFP4 M=1 decode steps (8 rotating weight copies), for rocprofv3")
     ap.add_argument("--json-out", default=None)
     return ap.parse_args()
 
@@ -304,6 +306,20 @@ def main():
                              workspace=ws)
         torch.cuda.synchronize()
         log(f"prefill counter steps done: {args.prefill_counters}")
+        return
+
+    if args.decode_counters:
+        blk, gs = nvfp4_weights(torch, wq, synth, dev)
+        sets = [blk] + [{n: t.clone() for n, t in blk.items()} for _ in range(7)]
+        xb, _ = synth.nvfp4_x(1)
+        x = torch.from_numpy(xb.view("int16")).to(dev).view(torch.bfloat16)
+        out = torch.empty((1, H), dtype=torch.float32, device=dev)
+        ws = torch.empty(wq.mlp_workspace_bytes(wq.WQ_FMT_NVFP4, 1, H, I), dtype=torch.uint8, device=dev)
+        for i in range(args.decode_counters):
+            b = sets[i % 8]
+            wq.mlp_nvfp4_run(x, b["gate"], gs["gate"], b["up"], gs["up"], b["down"], gs["down"], out=out, workspace=ws)
+        torch.cuda.synchronize()
+        log(f"nvfp4 decode counter steps done: {args.decode_counters}")
         return
 
     K, W = args.steps, args.warmup
