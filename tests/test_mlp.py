@@ -153,7 +153,7 @@ def test_nvfp4_paths_agree_with_oracle(nv_big, M):
     assert np.array_equal(host(nv_run(dblk, gs, bf16_dev(xb))).view(np.uint32), ys[want].view(np.uint32))
 
 
-@pytest.mark.parametrize("M", [12, 16, 48])
+@pytest.mark.parametrize("M", [2, 12, 33, 128])
 def test_fp8_short_batch_paths_agree_with_oracle(fp8_big, M):
     d = fp8_big
     xb = synth.to_bf16_bits(np.random.default_rng(500 + M).standard_normal((M, 5120)).astype(np.float32))
@@ -163,7 +163,7 @@ def test_fp8_short_batch_paths_agree_with_oracle(fp8_big, M):
     for path in ("gemv", "mfma"):
         ys[path] = host(wq.mlp_fp8w_run(bf16_dev(xb), *W, path=path))
         gate(ys[path], ref, what=f"fp8 M={M} {path}")
-    want = "gemv" if M < 13 else "mfma"                      # WQ_NARROW_MIN_ROWS_FP8
+    want = "gemv" if M < 2 else "mfma"                       # WQ_NARROW_MIN_ROWS_FP8
     assert np.array_equal(host(wq.mlp_fp8w_run(bf16_dev(xb), *W)).view(np.uint32), ys[want].view(np.uint32))
 
 

@@ -21,25 +21,23 @@
 // Tiling (both kernels): a workgroup of 4 waves computes a (32*MB) x 128 output tile (of both gate and
 // up for the fused projection).  All waves share the activation tile, staged in LDS; each wave owns 32
 // output columns and decodes its own weight fragments into registers, so every decoded fragment feeds
-// MB (x2 with gate+up) MFMAs.  K is walked in steps of 64 (one Block64 record per column).
+// MB (x2 with gate+up) MFMAs.  K is walked in steps of 64.
 //
-// FP8 weights (mfma_gemm_kernel): activation rows padded to 144 bytes in LDS; weight bytes loaded
-// straight from global memory into registers one K step ahead.
-//
-// NVFP4 weights (nv_gemm_kernel): a lane-per-column load of 36-byte records touches one cache line per
-// lane, and that access pattern, not bandwidth, limited the register-load form.  Here both operands move
-// by direct global->LDS copies (global_load_lds_dwordx4) in a coalesced order: the activation tile
+// Copy-fed GEMM (nv_gemm_kernel, both formats, K >= 256 for NVFP4 and K >= 128 for FP8): a lane-per-
+// column load of weight bytes touches one cache line per lane, and that access pattern, not bandwidth,
+// limited the register-load form (mfma_gemm_kernel, kept for shorter K).  Here both operands move by
+// direct global->LDS copies (global_load_lds_dwordx4) in a coalesced order: the activation tile
 // (128-byte rows, 16-byte chunk c of row r stored at chunk c ^ (r & 7), so fragment reads are
-// bank-conflict free) in a 2-stage ring, and the weights in blocks of 4 records per column (144
-// contiguous bytes = 9 chunks, 16-byte aligned in the row), one block buffer per wave.  At the start of
-// a block each wave reads the whole block of its columns into registers and immediately refills the
-// buffer with the next block, so the weight copy has four K steps to land.  Inside a K step the
-// activation fragments of sub-step s+1 are read while the MFMAs of sub-step s run; the single barrier
-// per K step sits after the third sub-step.  Two workgroups share a CU (at most 72 KB of LDS each).
-// Batches of at most 32 or 64 rows run 32- or 64-row tiles (MB = 1, 2), so a short batch streams the
-// weights once with little padding; the split-K plan below then spreads the few tiles over the chip.
-// A 32-row tile's K step is too short to cover a memory round trip, so those tiles copy the
-// activations of a whole 4-record block with its weights and wait once per block (block schedule).
+// bank-conflict free) in a 2-stage ring, and the weights in blocks per column (NVFP4: 4 records = 144
+// contiguous bytes; FP8: 2 K steps = 128 code bytes, chunk-swizzled), one block buffer per wave.  At
+// the start of a block each wave reads the whole block of its columns into registers and immediately
+// refills the buffer with the next block, so the weight copy has the block's K steps to land.  Inside
+// a K step the activation fragments of sub-step s+1 are read while the MFMAs of sub-step s run; the
+// single barrier per K step sits after the third sub-step.  Two workgroups share a CU (at most 72 KB of
+// LDS each).  Batches of at most 32 or 64 rows run 32- or 64-row tiles (MB = 1, 2), so a short batch
+// streams the weights once with little padding; the split-K plan below then spreads the few tiles over
+// the chip.  A 32-row tile's K step is too short to cover a memory round trip, so those tiles copy the
+// activations of a whole block with its weights and wait once per block (block schedule).
 //
 // MFMA v_mfma_f32_32x32x16_f16 operand layout (checked on gfx950): A lane l holds row
 // l%32, k = 8*(l/32) + j; B lane l holds column l%32, same k; D register r of lane l
@@ -345,13 +343,24 @@ __global__ void __launch_bounds__(256, 2) mfma_gemm_kernel(int M, int K, int N, 
 
 // ---- NVFP4: operands by global->LDS copy (lds_copy16 / wait_vmem / wait_lds in dev_common.h) -----
 
-// MB = 1, 2, 4: 32-, 64- or 128-row tiles (the narrow ones for M < 97)
+// Weight blocks of the copy-fed GEMM, by format: KSB K steps (64 k each) per block, CB bytes of one
+// column per block, CPM copy instructions per matrix and wave (32 columns), MBYTES of LDS per matrix and
+// wave.  NVFP4 (FMT 1): 4 Block64 records = 144 bytes = 9 chunks per column (288 slots, 32 pad slots).
+// FP8 (FMT 0): 2 K steps = 128 code bytes = 8 chunks per column (256 slots).
+template <int FMT> struct WGeo;
+template <> struct WGeo<1> { static constexpr int KSB = 4, CB = 144, CPM = 5, MBYTES = 5120; };
+template <> struct WGeo<0> { static constexpr int KSB = 2, CB = 128, CPM = 4, MBYTES = 4096; };
+// MB = 1, 2, 4: 32-, 64- or 128-row tiles
 constexpr int nv_astage(int mb) { return 32 * mb * 128; }   // bytes per activation stage
-constexpr int nv_wave_wbytes(bool gu) { return (gu ? 2 : 1) * 5 * 1024; }
-// Activation stages in the LDS ring: 2 (one per K step, stepped schedule) or 8 (two 4-step blocks,
-// block schedule)
-constexpr int nv_astages(bool bs) { return bs ? 8 : 2; }
-constexpr int nv_lds_bytes(bool gu, int mb, bool bs) { return nv_astages(bs) * nv_astage(mb) + 4 * nv_wave_wbytes(gu); }
+template <int FMT> constexpr int g_wave_wbytes(bool gu) { return (gu ? 2 : 1) * WGeo<FMT>::MBYTES; }
+// Activation stages in the LDS ring: 2 (one per K step, stepped schedule) or two blocks' worth (block
+// schedule)
+template <int FMT> constexpr int g_astages(bool bs) { return bs ? 2 * WGeo<FMT>::KSB : 2; }
+template <int FMT> constexpr int g_lds_bytes(bool gu, int mb, bool bs) {
+  return g_astages<FMT>(bs) * nv_astage(mb) + 4 * g_wave_wbytes<FMT>(gu);
+}
+// Smallest K the copy-fed GEMM takes (the short last block is copied as the row's last CB bytes).
+constexpr int g_min_k(int fmt) { return fmt == 1 ? 256 : 128; }
 // Tile rows / 32 for an M-row launch.  The down projection (long K, short N) keeps 32-row tiles up to
 // M = 128: re-reading its weights once per 32 rows costs less than the stepped schedule's waits.
 inline int nv_mb(int M, bool gu) {
@@ -362,7 +371,7 @@ inline int nv_mb(int M, bool gu) {
 // Work plan of one launch, a pure function of the shape.  (32*MB)x128 tiles; with two workgroups on each
 // of the 256 CUs there are 512 slots.  When the last round of tiles would leave most slots idle (or
 // there are fewer tiles than slots at all) the tiles of that round are split along K into S parts of
-// whole 4-record weight blocks: the parts run first, store raw float32 partial tiles, and a second
+// whole weight blocks: the parts run first, store raw float32 partial tiles, and a second
 // kernel adds the S parts of every element in part order and applies the epilogue.  The sum order
 // is fixed by the shape, so results are reproducible.
 constexpr int kNvSlots = 512;
@@ -374,14 +383,15 @@ struct NvPlan {
   int S, bps;            // split tiles [full, tiles) run as S parts of bps blocks (S = 1: none)
   int units, units_grid; // (tiles - full) * S parts; rounded up to a multiple of 8
 };
-// slots: concurrent workgroups; smax: most K parts per tile; mb: tile rows / 32 (0: nv_mb(M))
-inline NvPlan nv_plan_ex(int M, int K, int N, bool gu, int slots, int smax, int mb = 0) {
+// ksb: K steps per weight block; slots: concurrent workgroups; smax: most K parts per tile; mb: tile rows
+// / 32 (0: nv_mb(M))
+inline NvPlan nv_plan_ex(int M, int K, int N, bool gu, int ksb, int slots, int smax, int mb = 0) {
   NvPlan p{};
   p.bm = 32 * (mb > 0 ? mb : nv_mb(M, gu));
   p.ntm = (M + p.bm - 1) / p.bm;
   p.ntn = (N + 127) / 128;
   p.tiles = p.ntm * p.ntn;
-  const int nblk = (K / 64 + 3) / 4;
+  const int nblk = (K / 64 + ksb - 1) / ksb;
   int tail = 0;
   {
     if (p.tiles < slots) {
@@ -411,26 +421,34 @@ inline NvPlan nv_plan_ex(int M, int K, int N, bool gu, int slots, int smax, int 
   p.units_grid = (p.units + 7) / 8 * 8;
   return p;
 }
-inline NvPlan nv_plan(int M, int K, int N, bool gu) { return nv_plan_ex(M, K, N, gu, kNvSlots, 8); }
+inline NvPlan nv_plan(int fmt, int M, int K, int N, bool gu) {
+  return nv_plan_ex(M, K, N, gu, fmt == 1 ? WGeo<1>::KSB : WGeo<0>::KSB, kNvSlots, 8);
+}
 inline size_t nv_partial_bytes(const NvPlan& p, bool gu) {
   return (size_t)p.units * (gu ? 2 : 1) * p.bm * 128 * 4;
 }
 
-template <bool GU, int MB, bool BS>
+// FMT 1: NVFP4 Block64 weights, column factor inv0 / inv1.  FMT 0: FP8 E4M3 codes [N][K], column scales
+// cs0[n] / cs1[n].
+template <int FMT, bool GU, int MB, bool BS>
 __global__ void __launch_bounds__(256, 2) nv_gemm_kernel(int M, int K, int N, NvPlan plan,
                                                         const uint16_t* __restrict__ a16,
                                                         const float* __restrict__ rowscale,
-                                                        const uint8_t* __restrict__ w0, float inv0,
-                                                        const uint8_t* __restrict__ w1, float inv1,
+                                                        const uint8_t* __restrict__ w0, const float* __restrict__ cs0,
+                                                        float inv0, const uint8_t* __restrict__ w1,
+                                                        const float* __restrict__ cs1, float inv1,
                                                         void* __restrict__ out, float* __restrict__ partials) {
+  using Geo = WGeo<FMT>;
+  constexpr int KSB = Geo::KSB, CB = Geo::CB, CPM = Geo::CPM, MBYTES = Geo::MBYTES;
   constexpr int NM = GU ? 2 : 1;
   constexpr int kNvAStage = nv_astage(MB);
-  constexpr int AS = nv_astages(BS);
+  constexpr int AS = g_astages<FMT>(BS);
+  constexpr int AMASK = AS - 1;                // stage of K step kt under the block schedule: kt & AMASK
   constexpr int PT = 32 * MB * 128;            // elements of one partial tile per matrix
-  constexpr int NW = NM * 5;                   // weight copies per wave per block: 288 chunks (+32 pad) per matrix
+  constexpr int NW = NM * CPM;                 // weight copies per wave per block
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int nk = K >> 6;
-  const int nblk = (nk + 3) >> 2;
+  const int nblk = (nk + KSB - 1) / KSB;
   // Workgroups [0, units_grid) run the K parts of the split tiles (dispatched first, so they finish
   // early); the rest run whole tiles in an XCD-aware order: workgroup b runs on XCD b % 8, and each XCD
   // gets a contiguous run of tiles (n fastest) so the activation band it works on stays in its L2.
@@ -448,7 +466,7 @@ __global__ void __launch_bounds__(256, 2) nv_gemm_kernel(int M, int K, int N, Nv
     tile = (f & 7) * per + (f >> 3);
     if (tile >= plan.full) return;
   }
-  const int kt0 = 4 * kb0, kt1 = min(4 * kb1, nk);
+  const int kt0 = KSB * kb0, kt1 = min(KSB * kb1, nk);
   const int ntn = plan.ntn;
   const int tm = tile / ntn;
   const int tn = tile - tm * ntn;
@@ -459,10 +477,10 @@ __global__ void __launch_bounds__(256, 2) nv_gemm_kernel(int M, int K, int N, Nv
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 31;
   const int h = lane >> 5;
-  const uint32_t rb = (uint32_t)nk * 36u;      // bytes per weight row
+  const uint32_t rb = FMT == 1 ? (uint32_t)nk * 36u : (uint32_t)K;   // bytes per weight row
   const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
-  const uint32_t wlds = lds0 + AS * kNvAStage + wave * nv_wave_wbytes(GU);
-  const uint8_t* wbuf = lds + AS * kNvAStage + wave * nv_wave_wbytes(GU);
+  const uint32_t wlds = lds0 + AS * kNvAStage + wave * g_wave_wbytes<FMT>(GU);
+  const uint8_t* wbuf = lds + AS * kNvAStage + wave * g_wave_wbytes<FMT>(GU);
 
   // Activation chunk p = tid + 256 i: tile row p >> 3, LDS chunk p & 7, global chunk (p & 7) ^ (row & 7).
   uint32_t aoff[MB];
@@ -471,15 +489,24 @@ __global__ void __launch_bounds__(256, 2) nv_gemm_kernel(int M, int K, int N, Nv
     const int p = tid + 256 * i, row = p >> 3, c = p & 7;
     aoff[i] = (uint32_t)min(m0 + row, M - 1) * (uint32_t)K * 2u + (uint32_t)((c ^ (row & 7)) * 16);
   }
-  // Weight copy j = 5 t + i of matrix t, slot s = 64 i + lane (slots 288..319 re-read chunks of slots
-  // 0..31): column c = s / 9 of this wave, chunk q = s % 9 of the column's 144-byte block.  The block of
-  // column c of matrix t sits at LDS wbuf + 5120 t + 144 c.
+  // Weight copy j = CPM t + i of matrix t writes LDS slot s = 64 i + lane of the matrix's block buffer
+  // (wbuf + MBYTES t).  NVFP4: column c = s / 9, chunk q = s % 9 of the column's 144-byte block (slots
+  // 288..319 re-read chunks of slots 0..31), the column's block at 144 c.  FP8: column c = s / 8, slot
+  // position p = s % 8 holds chunk p ^ ((c / 2) % 8) of the column's 128-byte block (a swizzle that keeps
+  // the 16-byte fragment reads of 16 consecutive columns on distinct banks), the column's block at 128 c.
   uint32_t woff[NW];
 #pragma unroll
   for (int j = 0; j < NW; ++j) {
-    int s = 64 * (j % 5) + lane;
-    if (s >= 288) s -= 288;
-    const int c = s / 9, q = s - 9 * c;
+    int s = 64 * (j % CPM) + lane;
+    int c, q;
+    if constexpr (FMT == 1) {
+      if (s >= 288) s -= 288;
+      c = s / 9;
+      q = s - 9 * c;
+    } else {
+      c = s >> 3;
+      q = (s & 7) ^ ((c >> 1) & 7);
+    }
     woff[j] = (uint32_t)min(n0 + 32 * wave + c, N - 1) * rb + 16u * (uint32_t)q;
   }
   auto copy_a = [&](int kt, int stage) {
@@ -489,16 +516,16 @@ __global__ void __launch_bounds__(256, 2) nv_gemm_kernel(int M, int K, int N, Nv
 #pragma unroll
     for (int i = 0; i < MB; ++i) lds_copy16(aoff[i], base, __builtin_amdgcn_readfirstlane(sb + (256 * i + 64 * wave) * 16));
   };
-  // A row whose record count r = nk % 4 is not 0 ends in a short block: it is copied as the last 144
-  // bytes of the row (records 4 - r .. 3 of the window are the valid ones; K >= 256, so the window starts
-  // inside the row) and read_block moves those records down to positions 0 .. r-1.
-  const int rtail = nk & 3;
+  // A row whose K-step count r = nk % KSB is not 0 ends in a short block: it is copied as the last CB
+  // bytes of the row (steps KSB - r .. KSB - 1 of the window are the valid ones; K >= g_min_k, so the
+  // window starts inside the row) and read_block moves those steps down to positions 0 .. r-1.
+  const int rtail = nk % KSB;
   auto copy_w = [&](int blk) {
     blk = min(blk, nblk - 1);
-    const uint32_t boff = (rtail && blk == nblk - 1) ? rb - 144u : (uint32_t)blk * 144u;
+    const uint32_t boff = (rtail && blk == nblk - 1) ? rb - (uint32_t)CB : (uint32_t)blk * CB;
 #pragma unroll
     for (int j = 0; j < NW; ++j)
-      lds_copy16(woff[j] + boff, j < 5 ? w0 : w1, __builtin_amdgcn_readfirstlane(wlds + 1024 * j));
+      lds_copy16(woff[j] + boff, j < CPM ? w0 : w1, __builtin_amdgcn_readfirstlane(wlds + 1024 * j));
   };
 
   f32x16 acc[NM][MB];
@@ -509,42 +536,64 @@ __global__ void __launch_bounds__(256, 2) nv_gemm_kernel(int M, int K, int N, Nv
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[t][mb][r] = 0.f;
 
-  // Registers of one 4-record block for this lane's column of matrix t: record J's scale dword and the
-  // 16 nibble bytes of its half h (bytes 36 J + 4 + 16 h .. + 15 of the block).
-  struct WBlock { uint32_t nib[4][4]; uint32_t d[4]; };
-  auto shift_block = [&](WBlock* wb, auto Sc) {   // record J <- record J + S
+  // Registers of one weight block for this lane's column of matrix t.  NVFP4: record J's scale dword and
+  // the 16 nibble bytes of its half h (bytes 36 J + 4 + 16 h .. + 15 of the block).  FP8: the code bytes of
+  // K step J, half h (bytes 64 J + 32 h .. + 31), as two chunks.
+  struct WBlockNv { uint32_t nib[4][4]; uint32_t d[4]; };
+  struct WBlockF8 { u32x4 c[2][2]; };
+  using WBlock = std::conditional_t<FMT == 1, WBlockNv, WBlockF8>;
+  auto shift_block = [&](WBlock* wb, auto Sc) {   // step J <- step J + S
     constexpr int S = decltype(Sc)::value;
 #pragma unroll
     for (int t = 0; t < NM; ++t)
 #pragma unroll
-      for (int J = 0; J + S < 4; ++J) {
-        wb[t].d[J] = wb[t].d[J + S];
+      for (int J = 0; J + S < KSB; ++J) {
+        if constexpr (FMT == 1) {
+          wb[t].d[J] = wb[t].d[J + S];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) wb[t].nib[J][e] = wb[t].nib[J + S][e];
+          for (int e = 0; e < 4; ++e) wb[t].nib[J][e] = wb[t].nib[J + S][e];
+        } else {
+          wb[t].c[J][0] = wb[t].c[J + S][0];
+          wb[t].c[J][1] = wb[t].c[J + S][1];
+        }
       }
   };
   auto read_block = [&](WBlock* wb, int blk) {
 #pragma unroll
     for (int t = 0; t < NM; ++t) {
-      const uint8_t* bp = wbuf + 5120 * t + 144 * li;
+      if constexpr (FMT == 1) {
+        const uint8_t* bp = wbuf + MBYTES * t + 144 * li;
 #pragma unroll
-      for (int J = 0; J < 4; ++J) wb[t].d[J] = *reinterpret_cast<const uint32_t*>(bp + 36 * J);
-      u32x4 P = *reinterpret_cast<const u32x4*>(bp + 16 * h);          // record 0: chunks h, h+1
-      u32x4 Q = *reinterpret_cast<const u32x4*>(bp + 16 * (1 + h));
-      wb[t].nib[0][0] = P.y; wb[t].nib[0][1] = P.z; wb[t].nib[0][2] = P.w; wb[t].nib[0][3] = Q.x;
-      P = *reinterpret_cast<const u32x4*>(bp + 16 * (2 + h));               // record 1: chunks 2+h, 3+h
-      Q = *reinterpret_cast<const u32x4*>(bp + 16 * (3 + h));
-      wb[t].nib[1][0] = P.z; wb[t].nib[1][1] = P.w; wb[t].nib[1][2] = Q.x; wb[t].nib[1][3] = Q.y;
-      P = *reinterpret_cast<const u32x4*>(bp + 16 * (4 + h));               // record 2: chunks 4+h, 5+h
-      Q = *reinterpret_cast<const u32x4*>(bp + 16 * (5 + h));
-      wb[t].nib[2][0] = P.w; wb[t].nib[2][1] = Q.x; wb[t].nib[2][2] = Q.y; wb[t].nib[2][3] = Q.z;
-      P = *reinterpret_cast<const u32x4*>(bp + 16 * (7 + h));               // record 3: chunk 7+h
-      wb[t].nib[3][0] = P.x; wb[t].nib[3][1] = P.y; wb[t].nib[3][2] = P.z; wb[t].nib[3][3] = P.w;
+        for (int J = 0; J < 4; ++J) wb[t].d[J] = *reinterpret_cast<const uint32_t*>(bp + 36 * J);
+        u32x4 P = *reinterpret_cast<const u32x4*>(bp + 16 * h);          // record 0: chunks h, h+1
+        u32x4 Q = *reinterpret_cast<const u32x4*>(bp + 16 * (1 + h));
+        wb[t].nib[0][0] = P.y; wb[t].nib[0][1] = P.z; wb[t].nib[0][2] = P.w; wb[t].nib[0][3] = Q.x;
+        P = *reinterpret_cast<const u32x4*>(bp + 16 * (2 + h));               // record 1: chunks 2+h, 3+h
+        Q = *reinterpret_cast<const u32x4*>(bp + 16 * (3 + h));
+        wb[t].nib[1][0] = P.z; wb[t].nib[1][1] = P.w; wb[t].nib[1][2] = Q.x; wb[t].nib[1][3] = Q.y;
+        P = *reinterpret_cast<const u32x4*>(bp + 16 * (4 + h));               // record 2: chunks 4+h, 5+h
+        Q = *reinterpret_cast<const u32x4*>(bp + 16 * (5 + h));
+        wb[t].nib[2][0] = P.w; wb[t].nib[2][1] = Q.x; wb[t].nib[2][2] = Q.y; wb[t].nib[2][3] = Q.z;
+        P = *reinterpret_cast<const u32x4*>(bp + 16 * (7 + h));               // record 3: chunk 7+h
+        wb[t].nib[3][0] = P.x; wb[t].nib[3][1] = P.y; wb[t].nib[3][2] = P.z; wb[t].nib[3][3] = P.w;
+      } else {
+        const uint8_t* bp = wbuf + MBYTES * t + 128 * li;
+        const int sw = (li >> 1) & 7;
+#pragma unroll
+        for (int J = 0; J < 2; ++J)
+#pragma unroll
+          for (int e = 0; e < 2; ++e)
+            wb[t].c[J][e] = *reinterpret_cast<const u32x4*>(bp + 16 * ((4 * J + 2 * h + e) ^ sw));
+      }
     }
     if (rtail && blk == nblk - 1) {
-      if (rtail == 1) shift_block(wb, std::integral_constant<int, 3>{});
-      else if (rtail == 2) shift_block(wb, std::integral_constant<int, 2>{});
-      else shift_block(wb, std::integral_constant<int, 1>{});
+      if constexpr (FMT == 1) {
+        if (rtail == 1) shift_block(wb, std::integral_constant<int, 3>{});
+        else if (rtail == 2) shift_block(wb, std::integral_constant<int, 2>{});
+        else shift_block(wb, std::integral_constant<int, 1>{});
+      } else {
+        shift_block(wb, std::integral_constant<int, 1>{});
+      }
     }
   };
   auto read_a = [&](int stage, int s, f16x8* af) {
@@ -553,17 +602,30 @@ __global__ void __launch_bounds__(256, 2) nv_gemm_kernel(int M, int K, int N, Nv
     for (int mb = 0; mb < MB; ++mb)
       af[mb] = *reinterpret_cast<const f16x8*>(ast + (32 * mb + li) * 128 + (((4 * h + s) ^ (li & 7)) * 16));
   };
-  // decode sub-step s of record J (exact f16: E2M1 x E4M3 group scale) and run its MFMAs
+  // decode sub-step s of step J into exact f16 (NVFP4: E2M1 x E4M3 group scale; FP8: the E4M3 codes)
+  // and run its MFMAs
   auto mfmas = [&](const WBlock* wb, int J, int s, const f16x8* af) {
     f16x8 bfr[NM];
 #pragma unroll
     for (int t = 0; t < NM; ++t) {
-      const f16x2 dsc = e4m3x2_f16<false>(wb[t].d[J] >> (16 * h));   // groups 2h, 2h+1
-      const uint32_t w = wb[t].nib[J][s];
-      const _Float16 g = (s < 2) ? dsc.x : dsc.y;
-      const f16x2 gg = {g, g};
-      const f16x2 p0 = e2m1x2_f16<0>(w) * gg, p1 = e2m1x2_f16<1>(w) * gg, p2 = e2m1x2_f16<2>(w) * gg,
-                  p3 = e2m1x2_f16<3>(w) * gg;
+      f16x2 p0, p1, p2, p3;
+      if constexpr (FMT == 1) {
+        const f16x2 dsc = e4m3x2_f16<false>(wb[t].d[J] >> (16 * h));   // groups 2h, 2h+1
+        const uint32_t w = wb[t].nib[J][s];
+        const _Float16 g = (s < 2) ? dsc.x : dsc.y;
+        const f16x2 gg = {g, g};
+        p0 = e2m1x2_f16<0>(w) * gg;
+        p1 = e2m1x2_f16<1>(w) * gg;
+        p2 = e2m1x2_f16<2>(w) * gg;
+        p3 = e2m1x2_f16<3>(w) * gg;
+      } else {
+        const u32x4 ch = wb[t].c[J][s >> 1];                           // bytes 8 s .. 8 s + 7 of the half
+        const uint32_t wa = (s & 1) ? ch.z : ch.x, wb2 = (s & 1) ? ch.w : ch.y;
+        p0 = e4m3x2_f16<false>(wa);
+        p1 = e4m3x2_f16<true>(wa);
+        p2 = e4m3x2_f16<false>(wb2);
+        p3 = e4m3x2_f16<true>(wb2);
+      }
       bfr[t] = f16x8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
     }
 #pragma unroll
@@ -594,7 +656,7 @@ __global__ void __launch_bounds__(256, 2) nv_gemm_kernel(int M, int K, int N, Nv
     wait_lds();
     copy_w(kb0 + 1);
     read_a(0, 0, af0);
-    // K step kt (stage kt & 1, record J of the block in registers).
+    // K step kt (stage kt & 1, step J of the block in registers).
     auto step = [&](int kt, auto Jc) {
       constexpr int J = decltype(Jc)::value;
       read_a(kt & 1, 1, af1);
@@ -606,8 +668,8 @@ __global__ void __launch_bounds__(256, 2) nv_gemm_kernel(int M, int K, int N, Nv
       read_a(kt & 1, 3, af1);
       mfmas(wb, J, 2, af0);
       __builtin_amdgcn_sched_barrier(0);
-      // Step kt+1's activations were copied at the previous barrier; at record 0 the copy of the next
-      // weight block (issued after them) may still be in flight.
+      // Step kt+1's activations were copied at the previous barrier; at step 0 of a block the copy of the
+      // next weight block (issued after them) may still be in flight.
       if constexpr (J == 0) wait_vmem<NW>();
       else wait_vmem<0>();
       __syncthreads();
@@ -616,26 +678,28 @@ __global__ void __launch_bounds__(256, 2) nv_gemm_kernel(int M, int K, int N, Nv
       __builtin_amdgcn_sched_barrier(0);
       mfmas(wb, J, 3, af1);
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (J == 3) {                  // next block: complete since the wait above
-        read_block(wb, (kt >> 2) + 1);
+      if constexpr (J == KSB - 1) {            // next block: complete since the wait above
+        read_block(wb, kt / KSB + 1);
         wait_lds();
-        copy_w((kt >> 2) + 2);
+        copy_w(kt / KSB + 2);
       }
     };
-    for (int kt = kt0; kt < kt1; kt += 4) {     // kt0 is a multiple of 4: record J = kt % 4
+    for (int kt = kt0; kt < kt1; kt += KSB) {   // kt0 is a multiple of KSB: step J = kt % KSB
       step(kt, std::integral_constant<int, 0>{});
       if (kt + 1 < kt1) step(kt + 1, std::integral_constant<int, 1>{});
-      if (kt + 2 < kt1) step(kt + 2, std::integral_constant<int, 2>{});
-      if (kt + 3 < kt1) step(kt + 3, std::integral_constant<int, 3>{});
+      if constexpr (KSB == 4) {
+        if (kt + 2 < kt1) step(kt + 2, std::integral_constant<int, 2>{});
+        if (kt + 3 < kt1) step(kt + 3, std::integral_constant<int, 3>{});
+      }
     }
   } else {
     // Block schedule (narrow tiles, whose K steps are too short to cover a memory round trip): the
-    // activations of a whole 4-step block are copied together with its weights, into an 8-stage ring
-    // (stage kt & 7), so the copies of block b+1 fly during all four steps of block b and the wait and
-    // the barrier come once per block.
+    // activations of a whole KSB-step block are copied together with its weights, into a ring of two
+    // blocks' stages (stage kt & AMASK), so the copies of block b+1 fly during all the steps of block b
+    // and the wait and the barrier come once per block.
     auto copy_a_blk = [&](int blk) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) copy_a(4 * blk + j, (4 * blk + j) & 7);
+      for (int j = 0; j < KSB; ++j) copy_a(KSB * blk + j, (KSB * blk + j) & AMASK);
     };
     copy_w(kb0);
     copy_a_blk(kb0);
@@ -647,10 +711,10 @@ __global__ void __launch_bounds__(256, 2) nv_gemm_kernel(int M, int K, int N, Nv
       copy_w(kb0 + 1);
       copy_a_blk(kb0 + 1);
     }
-    read_a(kt0 & 7, 0, af0);
+    read_a(kt0 & AMASK, 0, af0);
     auto bstep = [&](int kt, auto Jc) {
       constexpr int J = decltype(Jc)::value;
-      const int st = kt & 7;
+      const int st = kt & AMASK;
       read_a(st, 1, af1);
       mfmas(wb, J, 0, af0);
       __builtin_amdgcn_sched_barrier(0);
@@ -660,16 +724,18 @@ __global__ void __launch_bounds__(256, 2) nv_gemm_kernel(int M, int K, int N, Nv
       read_a(st, 3, af1);
       mfmas(wb, J, 2, af0);
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (J < 3) read_a((kt + 1) & 7, 0, af0);   // same block: landed
+      if constexpr (J < KSB - 1) read_a((kt + 1) & AMASK, 0, af0);   // same block: landed
       mfmas(wb, J, 3, af1);
       __builtin_amdgcn_sched_barrier(0);
     };
     for (int blk = kb0; blk < kb1; ++blk) {
-      const int kt = 4 * blk;
+      const int kt = KSB * blk;
       bstep(kt, std::integral_constant<int, 0>{});
       if (kt + 1 < kt1) bstep(kt + 1, std::integral_constant<int, 1>{});
-      if (kt + 2 < kt1) bstep(kt + 2, std::integral_constant<int, 2>{});
-      if (kt + 3 < kt1) bstep(kt + 3, std::integral_constant<int, 3>{});
+      if constexpr (KSB == 4) {
+        if (kt + 2 < kt1) bstep(kt + 2, std::integral_constant<int, 2>{});
+        if (kt + 3 < kt1) bstep(kt + 3, std::integral_constant<int, 3>{});
+      }
       if (blk + 1 < kb1) {
         wait_vmem<0>();                        // block blk+1's copies landed (this wave's) ...
         __syncthreads();                       // ... and every wave's; all are done with block blk
@@ -679,7 +745,7 @@ __global__ void __launch_bounds__(256, 2) nv_gemm_kernel(int M, int K, int N, Nv
           copy_w(blk + 2);
           copy_a_blk(blk + 2);
         }
-        read_a((4 * blk + 4) & 7, 0, af0);
+        read_a((KSB * blk + KSB) & AMASK, 0, af0);
       }
     }
   }
@@ -702,6 +768,8 @@ __global__ void __launch_bounds__(256, 2) nv_gemm_kernel(int M, int K, int N, Nv
 
   const int ncol = n0 + 32 * wave + li;
   if (ncol >= N) return;
+  const float c0 = FMT == 1 ? inv0 : cs0[ncol];
+  const float c1 = FMT == 1 ? inv1 : (GU ? cs1[ncol] : 0.f);
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
@@ -710,12 +778,12 @@ __global__ void __launch_bounds__(256, 2) nv_gemm_kernel(int M, int K, int N, Nv
       if (m < M) {
         const float rs = rowscale ? rowscale[m] : 1.0f;
         if constexpr (GU) {
-          const float g = acc[0][mb][r] * rs * inv0;
-          const float u = acc[1][mb][r] * rs * inv1;
+          const float g = acc[0][mb][r] * rs * c0;
+          const float u = acc[1][mb][r] * rs * c1;
           const _Float16 a = (_Float16)(silu_f32(g) * u);
           reinterpret_cast<uint16_t*>(out)[(size_t)m * N + ncol] = __builtin_bit_cast(uint16_t, a);
         } else {
-          reinterpret_cast<float*>(out)[(size_t)m * N + ncol] = acc[0][mb][r] * rs * inv0;
+          reinterpret_cast<float*>(out)[(size_t)m * N + ncol] = acc[0][mb][r] * rs * c0;
         }
       }
     }
@@ -724,9 +792,12 @@ __global__ void __launch_bounds__(256, 2) nv_gemm_kernel(int M, int K, int N, Nv
 
 // Epilogue of the split tiles: element (row, col) of split tile i adds its S parts in part order.
 // Workgroup b handles 256 elements of split tile b / (bm / 2) (a tile has bm * 128 elements).
+// Column factors as in the GEMM: cs0[n] / cs1[n] (FP8) when cs0 is not null, else inv0 / inv1.
 template <bool GU>
 __global__ void __launch_bounds__(256) nv_splitk_finish(int M, int N, NvPlan plan, const float* __restrict__ partials,
-                                                       const float* __restrict__ rowscale, float inv0, float inv1,
+                                                       const float* __restrict__ rowscale,
+                                                       const float* __restrict__ cs0, float inv0,
+                                                       const float* __restrict__ cs1, float inv1,
                                                        void* __restrict__ out) {
   constexpr int NM = GU ? 2 : 1;
   const int per_tile = plan.bm / 2;                    // workgroups per split tile
@@ -745,20 +816,22 @@ __global__ void __launch_bounds__(256) nv_splitk_finish(int M, int N, NvPlan pla
 #pragma unroll
     for (int t = 0; t < NM; ++t) acc[t] += p[(size_t)s * NM * pt + t * pt];
   const float rs = rowscale ? rowscale[m] : 1.0f;
+  const float c0 = cs0 ? cs0[n] : inv0;
   if constexpr (GU) {
-    const float g = acc[0] * rs * inv0;
-    const float u = acc[1] * rs * inv1;
+    const float c1 = cs0 ? cs1[n] : inv1;
+    const float g = acc[0] * rs * c0;
+    const float u = acc[1] * rs * c1;
     const _Float16 a = (_Float16)(silu_f32(g) * u);
     reinterpret_cast<uint16_t*>(out)[(size_t)m * N + n] = __builtin_bit_cast(uint16_t, a);
   } else {
-    reinterpret_cast<float*>(out)[(size_t)m * N + n] = acc[0] * rs * inv0;
+    reinterpret_cast<float*>(out)[(size_t)m * N + n] = acc[0] * rs * c0;
   }
 }
 
-template <bool GU, int MB, bool BS>
+template <int FMT, bool GU, int MB, bool BS>
 hipError_t nv_launch(int M, int K, int N, const NvPlan& plan, const uint16_t* a16, const float* rowscale,
-                     const uint8_t* w0, float inv0, const uint8_t* w1, float inv1, void* out, float* partials,
-                     hipStream_t st) {
+                     const uint8_t* w0, const float* cs0, float inv0, const uint8_t* w1, const float* cs1,
+                     float inv1, void* out, float* partials, hipStream_t st) {
   // up to 72 KB of dynamic LDS: raise the per-kernel limit once per device
   static std::atomic<uint64_t> raised{0};
   int dev = 0;
@@ -766,31 +839,39 @@ hipError_t nv_launch(int M, int K, int N, const NvPlan& plan, const uint16_t* a1
   if (e != hipSuccess) return e;
   const uint64_t bit = (uint64_t)1 << (dev & 63);
   if (!(raised.load() & bit)) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(nv_gemm_kernel<GU, MB, BS>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, nv_lds_bytes(GU, MB, BS));
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(nv_gemm_kernel<FMT, GU, MB, BS>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, g_lds_bytes<FMT>(GU, MB, BS));
     if (e != hipSuccess) return e;
     raised.fetch_or(bit);
   }
   const int grid = plan.units_grid + (plan.full + 7) / 8 * 8;
-  hipLaunchKernelGGL((nv_gemm_kernel<GU, MB, BS>), dim3(grid), dim3(256), nv_lds_bytes(GU, MB, BS), st, M, K, N, plan, a16,
-                     rowscale, w0, inv0, w1, inv1, out, partials);
+  hipLaunchKernelGGL((nv_gemm_kernel<FMT, GU, MB, BS>), dim3(grid), dim3(256), g_lds_bytes<FMT>(GU, MB, BS), st, M, K,
+                     N, plan, a16, rowscale, w0, cs0, inv0, w1, cs1, inv1, out, partials);
   return hipGetLastError();
 }
 
-template <bool GU>
+template <int FMT, bool GU>
 hipError_t nv_dispatch(int M, int K, int N, const uint16_t* a16, const float* rowscale, const uint8_t* w0,
-                       float inv0, const uint8_t* w1, float inv1, void* out, float* partials, hipStream_t st) {
-  const NvPlan plan = nv_plan(M, K, N, GU);
+                       const float* cs0, float inv0, const uint8_t* w1, const float* cs1, float inv1, void* out,
+                       float* partials, hipStream_t st) {
+  const NvPlan plan = nv_plan(FMT, M, K, N, GU);
   if (plan.units > 0 && partials == nullptr) return hipErrorInvalidValue;
+  if (FMT == 1) cs0 = cs1 = nullptr;
   hipError_t e;
   switch (plan.bm) {
-    case 32: e = nv_launch<GU, 1, true>(M, K, N, plan, a16, rowscale, w0, inv0, w1, inv1, out, partials, st); break;
-    case 64: e = nv_launch<GU, 2, false>(M, K, N, plan, a16, rowscale, w0, inv0, w1, inv1, out, partials, st); break;
-    default: e = nv_launch<GU, 4, false>(M, K, N, plan, a16, rowscale, w0, inv0, w1, inv1, out, partials, st); break;
+    case 32:
+      e = nv_launch<FMT, GU, 1, true>(M, K, N, plan, a16, rowscale, w0, cs0, inv0, w1, cs1, inv1, out, partials, st);
+      break;
+    case 64:
+      e = nv_launch<FMT, GU, 2, false>(M, K, N, plan, a16, rowscale, w0, cs0, inv0, w1, cs1, inv1, out, partials, st);
+      break;
+    default:
+      e = nv_launch<FMT, GU, 4, false>(M, K, N, plan, a16, rowscale, w0, cs0, inv0, w1, cs1, inv1, out, partials, st);
+      break;
   }
   if (e != hipSuccess || plan.units == 0) return e;
   hipLaunchKernelGGL((nv_splitk_finish<GU>), dim3((plan.tiles - plan.full) * (plan.bm / 2)), dim3(256), 0, st, M, N,
-                     plan, partials, rowscale, inv0, inv1, out);
+                     plan, partials, rowscale, cs0, inv0, cs1, inv1, out);
   return hipGetLastError();
 }
 
@@ -830,15 +911,16 @@ hipError_t launch_rowscale_f16(int M, int K, const void* x, XType xt, uint16_t* 
 }
 
 size_t mfma_partial_bytes(int fmt, int M, int K, int N, bool gu) {
-  if (fmt != 1 || K < 256 || M <= 0) return 0;
-  return nv_partial_bytes(nv_plan(M, K, N, gu), gu);
+  if (K < g_min_k(fmt) || M <= 0) return 0;
+  return nv_partial_bytes(nv_plan(fmt, M, K, N, gu), gu);
 }
 
 hipError_t launch_mfma_gateup(int fmt, int M, int K, int N, const uint16_t* x16, const float* rowscale,
                               const uint8_t* w0, const float* cs0, float inv0, const uint8_t* w1,
                               const float* cs1, float inv1, uint16_t* act16, float* partials, hipStream_t st) {
-  if (fmt == 1 && K >= 256)
-    return nv_dispatch<true>(M, K, N, x16, rowscale, w0, inv0, w1, inv1, act16, partials, st);
+  if (K >= g_min_k(fmt))
+    return fmt == 1 ? nv_dispatch<1, true>(M, K, N, x16, rowscale, w0, cs0, inv0, w1, cs1, inv1, act16, partials, st)
+                    : nv_dispatch<0, true>(M, K, N, x16, rowscale, w0, cs0, inv0, w1, cs1, inv1, act16, partials, st);
   if (fmt == 1)
     return gemm_dispatch<1, true>(M, K, N, x16, rowscale, w0, cs0, inv0, w1, cs1, inv1, act16, st);
   return gemm_dispatch<0, true>(M, K, N, x16, rowscale, w0, cs0, inv0, w1, cs1, inv1, act16, st);
@@ -847,7 +929,9 @@ hipError_t launch_mfma_gateup(int fmt, int M, int K, int N, const uint16_t* x16,
 hipError_t launch_mfma_linear(int fmt, int M, int K, int N, const uint16_t* a16, const float* rowscale,
                               const uint8_t* w, const float* cs, float inv, float* y, float* partials,
                               hipStream_t st) {
-  if (fmt == 1 && K >= 256) return nv_dispatch<false>(M, K, N, a16, rowscale, w, inv, nullptr, 0.f, y, partials, st);
+  if (K >= g_min_k(fmt))
+    return fmt == 1 ? nv_dispatch<1, false>(M, K, N, a16, rowscale, w, cs, inv, nullptr, nullptr, 0.f, y, partials, st)
+                    : nv_dispatch<0, false>(M, K, N, a16, rowscale, w, cs, inv, nullptr, nullptr, 0.f, y, partials, st);
   if (fmt == 1) return gemm_dispatch<1, false>(M, K, N, a16, rowscale, w, cs, inv, nullptr, nullptr, 0.f, y, st);
   return gemm_dispatch<0, false>(M, K, N, a16, rowscale, w, cs, inv, nullptr, nullptr, 0.f, y, st);
 }
