@@ -69,6 +69,21 @@ def test_fp8_decode_5120x17408(fp8_big):
     gate(y, ref, what="fp8 5120x17408 M=1")
 
 
+def test_fp8_prefill_M512_reproducible_sampled_rows(fp8_big):
+    # FP8 on the MFMA path at M=512: the split-K plan and its ordered finish give the same bits run to
+    # run; sampled rows (both ends of every 128-row band) match the oracle.
+    d = fp8_big
+    xb = synth.to_bf16_bits(np.random.default_rng(512).standard_normal((512, 5120)).astype(np.float32))
+    W = fp8_dev(d)
+    x = bf16_dev(xb)
+    y1 = host(wq.mlp_fp8w_run(x, *W))
+    y2 = host(wq.mlp_fp8w_run(x, *W))
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+    rows = np.array([0, 1, 126, 127, 128, 255, 256, 383, 384, 510, 511])
+    ref = oracle.mlp_fp8w_ref(oracle.bf16_bits_to_f64(xb[rows]), *(d[n] for n in FP8_NAMES))
+    gate(y1[rows], ref, what="fp8 M=512 sampled rows (mfma)")
+
+
 # ---- NVFP4 (H=5120, I=17408) ----------------------------------------------------------------------
 @pytest.fixture(scope="module")
 def nv_big():
@@ -169,7 +184,10 @@ def test_fp8_short_batch_paths_agree_with_oracle(fp8_big, M):
 
 # ---- ragged tails: partial m and n tiles ----------------------------------------------------------------
 @pytest.mark.parametrize("fmt", ["fp8", "nvfp4"])
-@pytest.mark.parametrize("M,H,I", [(129, 320, 192), (1, 320, 192), (130, 64, 64), (255, 576, 448)])
+# K = 64 takes the register-load GEMM for both formats; K = 128 / 192 / 320 / 448 the copy-fed one with
+# short last blocks (FP8: odd K-step counts; NVFP4 K >= 256: record counts not a multiple of 4).
+@pytest.mark.parametrize("M,H,I", [(129, 320, 192), (1, 320, 192), (130, 64, 64), (255, 576, 448), (40, 128, 256),
+                                   (7, 192, 320)])
 def test_tail_shapes(fmt, M, H, I):
     r = np.random.default_rng(M * 7 + H)
     x = r.standard_normal((M, H)).astype(np.float32)
