@@ -15,7 +15,8 @@ come from each stage captured alone into a graph of K launches over the same
 rotating weights, timed the same way.
 
 Extras measured the same way: NVFP4 decode, NVFP4 prefill at M=512 and 8192
-(MFMA utilisation), and the AWQ routed-expert step (hot and rotating experts).
+(MFMA utilisation), both formats at a short batch (M=8) and FP8 at M=512 on the
+MFMA path, and the AWQ routed-expert step (hot and rotating experts).
 The CPU oracle is timed on the host on a bounded sample as a baseline.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--extras all|none|a,b]
@@ -92,6 +93,30 @@ class GraphBench:
             e1.record(self.stream)
         t.cuda.synchronize()
         return e0.elapsed_time(e1) / 1e3
+
+
+def fp8_batch(torch, wq, synth, d, M, K, copies):
+    """FP8 MLP on M rows of the decode config's weights (path AUTO), R rotating weight copies."""
+    dev = torch.device("cuda:0")
+    names = ("w_gate", "s_gate", "w_up", "s_up", "w_down", "s_down")
+    base = [torch.from_numpy(d[n]).to(dev) for n in names]
+    sets = [base] + [[t.clone() for t in base] for _ in range(copies - 1)]
+    import numpy as np
+    xb = synth.to_bf16_bits(synth.rng(2, synth.T_X, (M,)).standard_normal((M, H), dtype=np.float32))
+    x = torch.from_numpy(xb.view("int16")).to(dev).view(torch.bfloat16)
+    out = torch.empty((M, H), dtype=torch.float32, device=dev)
+    ws = torch.empty(wq.mlp_workspace_bytes(wq.WQ_FMT_FP8W, M, H, I), dtype=torch.uint8, device=dev)
+
+    def step(i, stage=None):
+        wq.mlp_fp8w_run(x, *sets[i % copies], out=out, workspace=ws, stage=stage)
+
+    step(0)
+    torch.cuda.synchronize()
+    g = GraphBench(torch, step, K)
+    g.replay_timed()
+    t = g.replay_timed()
+    gu_ms, dn_ms = stage_times(torch, step, K)
+    return dict(t=t, K=K, M=M, gu_ms=gu_ms, dn_ms=dn_ms, copies=copies)
 
 
 def stage_times(torch, step, K):
@@ -336,9 +361,23 @@ def main():
 
     extras = {}
     want = set() if args.extras == "none" else (
-        {"nvfp4_decode", "nvfp4_prefill_512", "nvfp4_prefill_8192", "awq"} if args.extras == "all"
+        {"nvfp4_decode", "nvfp4_prefill_512", "nvfp4_prefill_8192", "nvfp4_batch8", "fp8_batch8", "fp8_prefill_512",
+         "awq"} if args.extras == "all"
         else set(args.extras.split(",")))
-    if want & {"nvfp4_decode", "nvfp4_prefill_512", "nvfp4_prefill_8192"}:
+    if want & {"fp8_batch8", "fp8_prefill_512"}:
+        fp8_bytes = 3 * H * I + 4 * (2 * I + H)
+        for M, key, steps, copies in ((8, "fp8_batch8", 200, 4), (512, "fp8_prefill_512", 60, 2)):
+            if key not in want:
+                continue
+            n = fp8_batch(torch, wq, synth, r["data"], M, steps, copies)
+            tfl = 2.0 * M * 3 * H * I * n["K"] / n["t"] / 1e12
+            extras[key] = dict(
+                us_per_step=round(n["t"] / n["K"] * 1e6, 2), tok_per_s=round(M * n["K"] / n["t"], 1),
+                weight_GBps=round(fp8_bytes * n["K"] / n["t"] / 1e9, 1), TFLOPs=round(tfl, 1),
+                mfma_frac_f16_peak=round(tfl / MFMA_F16_PEAK_TFLOPS, 4), gateup_us=round(n["gu_ms"] * 1e3, 2),
+                down_us=round(n["dn_ms"] * 1e3, 2), path="mfma", weight_copies=copies)
+            log(key, extras[key])
+    if want & {"nvfp4_decode", "nvfp4_prefill_512", "nvfp4_prefill_8192", "nvfp4_batch8"}:
         blk, gs = nvfp4_weights(torch, wq, synth, dev)
         nv_bytes = 3 * (H * I // 64 * 36)
         if "nvfp4_decode" in want:
@@ -348,6 +387,13 @@ def main():
                 tok_per_s=round(n["K"] / n["t"], 1), hbm_frac=round(nv_bytes * n["K"] / n["t"] / 1e9 / HBM_PEAK_GBS, 4),
                 gateup_us=round(n["gu_ms"] * 1e3, 3), down_us=round(n["dn_ms"] * 1e3, 3), weight_copies=n["copies"])
             log("nvfp4 decode", extras["nvfp4_decode_M1"])
+        if "nvfp4_batch8" in want:
+            n = nvfp4_run(torch, wq, synth, blk, gs, 8, 200, 8, 0.0)
+            extras["nvfp4_batch8"] = dict(
+                us_per_step=round(n["t"] / n["K"] * 1e6, 2), tok_per_s=round(8 * n["K"] / n["t"], 1),
+                weight_GBps=round(nv_bytes * n["K"] / n["t"] / 1e9, 1), gateup_us=round(n["gu_ms"] * 1e3, 2),
+                down_us=round(n["dn_ms"] * 1e3, 2), path="mfma", weight_copies=n["copies"])
+            log("nvfp4_batch8", extras["nvfp4_batch8"])
         for M, key, steps in ((512, "nvfp4_prefill_512", 60), (8192, "nvfp4_prefill_8192", 12)):
             if key not in want:
                 continue
