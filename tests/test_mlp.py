@@ -110,6 +110,20 @@ def test_nvfp4_decode_M1(nv_big):
     gate(y, nv_ref(W, oracle.bf16_bits_to_f64(xb)), what="nvfp4 M=1")
 
 
+def test_nvfp4_gemv_rows_independent_of_M(nv_big):
+    # The GEMV path's fixed order: row m of a 5-row call (a 3-row and a 2-row pass over the weights in the
+    # down projection) equals the 1-row call on row m, bit for bit; two runs agree.
+    blk, gs, W, dblk = nv_big
+    xb, _ = synth.nvfp4_x(5, config_id=11)
+    x = bf16_dev(xb)
+    y5 = host(nv_run(dblk, gs, x, path="gemv"))
+    assert np.array_equal(y5.view(np.uint32), host(nv_run(dblk, gs, x, path="gemv")).view(np.uint32))
+    for m in range(5):
+        y1 = host(nv_run(dblk, gs, x[m:m + 1].contiguous(), path="gemv"))
+        assert np.array_equal(y1[0].view(np.uint32), y5[m].view(np.uint32)), m
+    gate(y5, nv_ref(W, oracle.bf16_bits_to_f64(xb)), what="nvfp4 M=5 gemv")
+
+
 def test_nvfp4_gpu_packer_feeds_the_mlp(nv_big):
     blk, gs, W, dblk = nv_big
     w = synth.nvfp4_mlp_weights()
@@ -164,7 +178,7 @@ def test_nvfp4_paths_agree_with_oracle(nv_big, M):
         ys[path] = host(nv_run(dblk, gs, bf16_dev(xb), path=path))
         gate(ys[path], ref, what=f"nvfp4 M={M} {path}")
     # AUTO takes the GEMV below WQ_NARROW_MIN_ROWS_NVFP4 rows and the MFMA GEMM from there on
-    want = "gemv" if M < 3 else "mfma"
+    want = "gemv" if M < 4 else "mfma"
     assert np.array_equal(host(nv_run(dblk, gs, bf16_dev(xb))).view(np.uint32), ys[want].view(np.uint32))
 
 

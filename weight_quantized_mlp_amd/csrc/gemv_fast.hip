@@ -592,23 +592,54 @@ __global__ void __launch_bounds__(64 * kItemWaves, 8) nv_lin_grp(int M, int K, i
 // A 16-wave workgroup owns kR32Rows output rows, interleaved over the grid (local row i is row
 // blockIdx + gridDim * i), so the rows the chip streams at any moment sit in two narrow windows of the
 // matrix.  Work item (row i, slot t) = the 32 records [32 t, 32 t + 32) of the row, 1152 contiguous
-// bytes; items are dealt round-robin to the waves.  Both the activation row and the items move by
+// bytes; items are dealt round-robin to the waves.  Both the activation rows and the items move by
 // global->LDS copies (kR32Depth items in flight per wave, explicit vmcnt waits): register loads of
 // the same data made the compiler wait for every outstanding load at the top of the item loop.
+// MR activation rows share one pass over the weights (each item is decoded once and used for all MR
+// rows); a call with more rows makes ceil(M / MR) passes.
 // Lane l of an item owns groups 2l, 2l+1 (record l / 2, 16 nibble bytes and 2 scale bytes).
-// Accumulation order (fixed; M-independent): per lane, group 2l then 2l+1, each a 16-weight partial in
-// ascending k times its E4M3 scale; per wave and row, items ascending, a 64-lane sum (wave64_sum) when
-// the wave leaves the row; per row, the 16 wave partials in wave order; times inv.
-constexpr int kR32Rows = 20, kR32Depth = 2, kR32Item = 1152;
-constexpr size_t r32_lds_bytes(int K) { return (size_t)K * 2 + (size_t)kItemWaves * kR32Depth * kR32Item; }
+// Accumulation order (fixed; independent of M and MR): per lane, group 2l then 2l+1, each a 16-weight
+// partial in ascending k times its E4M3 scale; per wave and row, items ascending, a 64-lane sum
+// (wave64_sum) when the wave leaves the row; per row, the 16 wave partials in wave order; times inv.
+constexpr int kR32Rows = 20, kR32Depth = 2, kR32Item = 1152, kR32MaxMR = 3;
+constexpr size_t r32_lds_bytes(int K, int MR) {
+  return (size_t)MR * K * 2 + (size_t)kItemWaves * kR32Depth * kR32Item;
+}
 
-template <bool F16, bool ONE>
+// 16 weights (8 nibble bytes in w0, w1, low nibble first) as eight 16-bit pairs in ascending k.
+template <bool F16>
+__device__ __forceinline__ void e2m1x16_decode(uint32_t w0, uint32_t w1, uint32_t* d) {
+  if constexpr (F16) {
+    d[0] = as_u32(e2m1x2_f16<0>(w0)); d[1] = as_u32(e2m1x2_f16<1>(w0));
+    d[2] = as_u32(e2m1x2_f16<2>(w0)); d[3] = as_u32(e2m1x2_f16<3>(w0));
+    d[4] = as_u32(e2m1x2_f16<0>(w1)); d[5] = as_u32(e2m1x2_f16<1>(w1));
+    d[6] = as_u32(e2m1x2_f16<2>(w1)); d[7] = as_u32(e2m1x2_f16<3>(w1));
+  } else {
+    d[0] = __builtin_bit_cast(uint32_t, e2m1x2_bf16<0>(w0)); d[1] = __builtin_bit_cast(uint32_t, e2m1x2_bf16<1>(w0));
+    d[2] = __builtin_bit_cast(uint32_t, e2m1x2_bf16<2>(w0)); d[3] = __builtin_bit_cast(uint32_t, e2m1x2_bf16<3>(w0));
+    d[4] = __builtin_bit_cast(uint32_t, e2m1x2_bf16<0>(w1)); d[5] = __builtin_bit_cast(uint32_t, e2m1x2_bf16<1>(w1));
+    d[6] = __builtin_bit_cast(uint32_t, e2m1x2_bf16<2>(w1)); d[7] = __builtin_bit_cast(uint32_t, e2m1x2_bf16<3>(w1));
+  }
+}
+// acc + sum of the 16 products of decoded pairs d[0..7] and activation pairs x0, x1 in ascending k
+template <bool F16>
+__device__ __forceinline__ float dot16_pairs(const uint32_t* d, u32x4 x0, u32x4 x1, float acc) {
+  const uint32_t xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if constexpr (F16) acc = dot2_f16(as_f16x2(d[i]), as_f16x2(xs[i]), acc);
+    else acc = dot2_bf16(__builtin_bit_cast(bf16x2, d[i]), xs[i], acc);
+  }
+  return acc;
+}
+
+template <bool F16, int MR>
 __global__ void __launch_bounds__(64 * kItemWaves) nv_lin_r32(int M, int K, int N, const uint16_t* __restrict__ xa,
                                                            const uint8_t* __restrict__ blk, float inv,
                                                            float* __restrict__ y) {
   constexpr int NW = kItemWaves, RB = kR32Rows, D = kR32Depth;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  __shared__ float part[NW][RB];
+  __shared__ float part[MR][NW][RB];
   const int U = K >> 5;                                // two-group units per row
   const int T = (U + 63) >> 6;                         // 32-record slots per row
   const uint32_t rb = (uint32_t)(K >> 6) * 36u;        // a multiple of 16
@@ -617,9 +648,9 @@ __global__ void __launch_bounds__(64 * kItemWaves) nv_lin_r32(int M, int K, int 
   const int NI = RB * T;
   const int nk = NI > wv ? (NI - wv + NW - 1) / NW : 0;
   const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
-  const uint32_t abytes = (uint32_t)K * 2u;
-  const uint32_t ring = lds0 + abytes + (uint32_t)wv * D * kR32Item;
-  const uint8_t* ringp = lds + abytes + wv * D * kR32Item;
+  const uint32_t abytes = (uint32_t)K * 2u;            // one activation row
+  const uint32_t ring = lds0 + MR * abytes + (uint32_t)wv * D * kR32Item;
+  const uint8_t* ringp = lds + MR * abytes + wv * D * kR32Item;
   auto rowof = [&](int i) { return (int)blockIdx.x + (int)gridDim.x * i; };
   // copies of an item: chunk c < 72 at 1152 t + 16 c of the row; chunks past the row's end (last slot)
   // are clamped to its last chunk: in bounds, and they belong to units >= U, never used
@@ -628,17 +659,21 @@ __global__ void __launch_bounds__(64 * kItemWaves) nv_lin_r32(int M, int K, int 
   const uint32_t qoff = (uint32_t)(lane >> 1) * 36u + 4u + 16u * (lane & 1);
   const uint32_t soff = (uint32_t)(lane >> 1) * 36u + 2u * (lane & 1);
   const int nslot = U * 4;                             // 16-byte activation pieces per row
-  const int Mloop = ONE ? 1 : M;
-  for (int m = 0; m < Mloop; ++m) {
-    if (m) __syncthreads();                            // the previous row's LDS reads are done
-    for (int i = threadIdx.x; i < NW * RB; i += blockDim.x) (&part[0][0])[i] = 0.f;
-    // activation row m, piece-major: LDS slot s = q U + u holds piece 4 u + q of the row
-    const uint16_t* xm = xa + (size_t)m * K;
-    for (int j = 0; 64 * (wv + NW * j) < nslot; ++j) {
-      const int sl = 64 * (wv + NW * j) + lane;
-      if (sl < nslot) {
-        const int q = sl / U, u = sl - q * U;
-        lds_copy16((uint32_t)(4 * u + q) * 16u, xm, __builtin_amdgcn_readfirstlane(lds0 + 1024u * (wv + NW * j)));
+  for (int m0 = 0; m0 < M; m0 += MR) {
+    if (m0) __syncthreads();                           // the previous pass's LDS reads are done
+    for (int i = threadIdx.x; i < MR * NW * RB; i += blockDim.x) (&part[0][0][0])[i] = 0.f;
+    // activation rows m0 .. m0+MR-1 (past M: row M-1 again, never stored), piece-major: LDS slot
+    // s = q U + u of row r holds piece 4 u + q of the row
+#pragma unroll
+    for (int r = 0; r < MR; ++r) {
+      const uint16_t* xm = xa + (size_t)min(m0 + r, M - 1) * K;
+      for (int j = 0; 64 * (wv + NW * j) < nslot; ++j) {
+        const int sl = 64 * (wv + NW * j) + lane;
+        if (sl < nslot) {
+          const int q = sl / U, u = sl - q * U;
+          lds_copy16((uint32_t)(4 * u + q) * 16u, xm,
+                     __builtin_amdgcn_readfirstlane(lds0 + r * abytes + 1024u * (wv + NW * j)));
+        }
       }
     }
     int lg = wv / T, lt = wv - (wv / T) * T, lk = 0;
@@ -657,13 +692,18 @@ __global__ void __launch_bounds__(64 * kItemWaves) nv_lin_r32(int M, int K, int 
     for (int d = 0; d < D; ++d) issue(d);
     wait_vmem<2 * D>();                                // this wave's activation copies landed ...
     __syncthreads();                                   // ... and every wave's
-    float acc = 0.f;
+    float acc[MR];
+#pragma unroll
+    for (int r = 0; r < MR; ++r) acc[r] = 0.f;
     int cur = -1;
     auto flush = [&]() {
       if (cur < 0) return;
-      const float v = wave64_sum(acc);
-      acc = 0.f;
-      if (lane == 0) part[wv][cur] = v;
+#pragma unroll
+      for (int r = 0; r < MR; ++r) {
+        const float v = wave64_sum(acc[r]);
+        acc[r] = 0.f;
+        if (lane == 0) part[r][wv][cur] = v;
+      }
     };
     int cg = wv / T, ct = wv - (wv / T) * T;
     for (int k = 0; k < nk; ++k) {
@@ -679,21 +719,22 @@ __global__ void __launch_bounds__(64 * kItemWaves) nv_lin_r32(int M, int K, int 
       if (u < U) {
         const uint8_t* sp = ringp + stage * kR32Item;
         const uint32_t* wp = reinterpret_cast<const uint32_t*>(sp + qoff);
-        const uint32_t w0 = wp[0], w1 = wp[1], w2 = wp[2], w3 = wp[3];
         const uint32_t sc = *reinterpret_cast<const uint16_t*>(sp + soff);
-        u32x4 xv[4];
+        uint32_t d0[8], d1[8];                         // groups 2l and 2l+1, decoded once for all rows
+        e2m1x16_decode<F16>(wp[0], wp[1], d0);
+        e2m1x16_decode<F16>(wp[2], wp[3], d1);
+        const float s0 = e4m3_byte_f32<0>(sc), s1 = e4m3_byte_f32<1>(sc);
 #pragma unroll
-        for (int qq = 0; qq < 4; ++qq) xv[qq] = *reinterpret_cast<const u32x4*>(lds + ((size_t)qq * U + u) * 16);
-        float p0, p1;
-        if constexpr (F16) {
-          p0 = dot16_e2m1_f16(w0, w1, xv[0], xv[1], 0.f);
-          p1 = dot16_e2m1_f16(w2, w3, xv[2], xv[3], 0.f);
-        } else {
-          p0 = dot16_e2m1_bf16(w0, w1, xv[0], xv[1], 0.f);
-          p1 = dot16_e2m1_bf16(w2, w3, xv[2], xv[3], 0.f);
+        for (int r = 0; r < MR; ++r) {
+          const uint8_t* ar = lds + r * abytes;
+          u32x4 xv[4];
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq) xv[qq] = *reinterpret_cast<const u32x4*>(ar + ((size_t)qq * U + u) * 16);
+          const float p0 = dot16_pairs<F16>(d0, xv[0], xv[1], 0.f);
+          const float p1 = dot16_pairs<F16>(d1, xv[2], xv[3], 0.f);
+          acc[r] = fmaf(p0, s0, acc[r]);
+          acc[r] = fmaf(p1, s1, acc[r]);
         }
-        acc = fmaf(p0, e4m3_byte_f32<0>(sc), acc);
-        acc = fmaf(p1, e4m3_byte_f32<1>(sc), acc);
       }
       wait_lds();                                      // the stage's LDS reads are done before its refill
       issue(stage);                                    // item k + D
@@ -704,9 +745,14 @@ __global__ void __launch_bounds__(64 * kItemWaves) nv_lin_r32(int M, int K, int 
     if (threadIdx.x < RB) {
       const int n = rowof(threadIdx.x);
       if (n < N) {
-        float v = 0.f;
-        for (int ww = 0; ww < NW; ++ww) v += part[ww][threadIdx.x];
-        y[(size_t)m * N + n] = v * inv;
+#pragma unroll
+        for (int r = 0; r < MR; ++r) {
+          if (m0 + r < M) {
+            float v = 0.f;
+            for (int ww = 0; ww < NW; ++ww) v += part[r][ww][threadIdx.x];
+            y[(size_t)(m0 + r) * N + n] = v * inv;
+          }
+        }
       }
     }
   }
@@ -733,7 +779,7 @@ bool fast_gemv_fp8_ok(int K, XType xt, bool gu) {
 bool fast_gemv_nvfp4_ok(int K, XType xt, bool gu) {
   if (K % 64) return false;
   if (gu) return xt == X_BF16 && (K / 16 + 63) / 64 <= 8;
-  if (xt != X_F32 && K % 256 == 0 && r32_lds_bytes(K) <= kMaxItemLds) return true;
+  if (xt != X_F32 && K % 256 == 0 && r32_lds_bytes(K, 1) <= kMaxItemLds) return true;
   return (size_t)K * (xt == X_F32 ? 4 : 2) <= kMaxItemLds;
 }
 
@@ -797,22 +843,27 @@ hipError_t launch_fast_nvfp4(int M, int K, int N, const void* x, XType xt, const
   }
   if (y16) return hipErrorInvalidValue;                // a single linear writes float32
   float* yf = reinterpret_cast<float*>(y);
-  if (xt != X_F32 && K % 256 == 0 && r32_lds_bytes(K) <= kMaxItemLds) {
-    const size_t lds = r32_lds_bytes(K);
+  if (xt != X_F32 && K % 256 == 0 && r32_lds_bytes(K, 1) <= kMaxItemLds) {
+    // rows per pass: as many as fit (at most kR32MaxMR), never more than M
+    int mr = 1;
+    while (mr < kR32MaxMR && mr < M && r32_lds_bytes(K, mr + 1) <= kMaxItemLds) ++mr;
+    const size_t lds = r32_lds_bytes(K, mr);
     const dim3 grid((N + kR32Rows - 1) / kR32Rows), block(64 * kItemWaves);
     const uint16_t* xb = reinterpret_cast<const uint16_t*>(x);
-#define WQ_LAUNCH(F, O)                                                                                      \
+#define WQ_LAUNCH(F, R)                                                                                      \
   do {                                                                                                       \
-    if (!lds_ok(nv_lin_r32<F, O>, lds)) return hipErrorInvalidValue;                                         \
-    hipLaunchKernelGGL((nv_lin_r32<F, O>), grid, block, lds, st, M, K, N, xb, b0, inv0, yf);                 \
+    if (!lds_ok(nv_lin_r32<F, R>, lds)) return hipErrorInvalidValue;                                         \
+    hipLaunchKernelGGL((nv_lin_r32<F, R>), grid, block, lds, st, M, K, N, xb, b0, inv0, yf);                 \
   } while (0)
-    if (xt == X_F16) {
-      if (M == 1) WQ_LAUNCH(true, true);
-      else WQ_LAUNCH(true, false);
-    } else {
-      if (M == 1) WQ_LAUNCH(false, true);
-      else WQ_LAUNCH(false, false);
-    }
+#define WQ_MR(F)                      \
+  do {                                \
+    if (mr == 1) WQ_LAUNCH(F, 1);     \
+    else if (mr == 2) WQ_LAUNCH(F, 2); \
+    else WQ_LAUNCH(F, 3);             \
+  } while (0)
+    if (xt == X_F16) WQ_MR(true);
+    else WQ_MR(false);
+#undef WQ_MR
 #undef WQ_LAUNCH
     return hipGetLastError();
   }
