@@ -405,11 +405,9 @@ Shape pick_shape(int N, size_t lds_bytes, int gran) {
   return best;
 }
 
-template <typename K>
-void set_lds_limit(K kernel, size_t bytes) {
-  if (bytes > 64 * 1024)
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-                              (int)bytes);
+template <auto KERN>
+bool lds_ok(size_t bytes) {
+  return bytes <= 64 * 1024 || raise_lds_limit<KERN>();
 }
 
 constexpr size_t kLdsBudget = 96 * 1024;  // activation staging per workgroup for multi-row slabs
@@ -424,13 +422,13 @@ hipError_t fp8_dispatch(int M, int K, int N, const void* x, const uint8_t* w0, c
   const Shape sh = pick_shape(N, lds, 1);
   constexpr int SEG = GU ? 5 : 6;
   if (slab4) {
-    auto kern = fp8w_gemv_kernel<XT, GU, 4, SEG>;
-    set_lds_limit(kern, lds);
+    constexpr auto kern = &fp8w_gemv_kernel<XT, GU, 4, SEG>;
+    if (!lds_ok<kern>(lds)) return hipErrorInvalidValue;
     hipLaunchKernelGGL(kern, dim3(sh.grid), dim3(sh.threads), lds, st, M, K, N, sh.rpw,
                        reinterpret_cast<const XT*>(x), w0, s0, w1, s1, y);
   } else {
-    auto kern = fp8w_gemv_kernel<XT, GU, 1, SEG>;
-    set_lds_limit(kern, lds);
+    constexpr auto kern = &fp8w_gemv_kernel<XT, GU, 1, SEG>;
+    if (!lds_ok<kern>(lds)) return hipErrorInvalidValue;
     hipLaunchKernelGGL(kern, dim3(sh.grid), dim3(sh.threads), lds, st, M, K, N, sh.rpw,
                        reinterpret_cast<const XT*>(x), w0, s0, w1, s1, y);
   }
@@ -447,13 +445,13 @@ hipError_t nvfp4_dispatch(int M, int K, int N, const void* x, const uint8_t* b0,
   const Shape sh = pick_shape(N, lds, 4);
   constexpr int SEG = GU ? 1 : 2;
   if (slab4) {
-    auto kern = nvfp4_gemv_kernel<XT, GU, 4, SEG, XF16, Y16>;
-    set_lds_limit(kern, lds);
+    constexpr auto kern = &nvfp4_gemv_kernel<XT, GU, 4, SEG, XF16, Y16>;
+    if (!lds_ok<kern>(lds)) return hipErrorInvalidValue;
     hipLaunchKernelGGL(kern, dim3(sh.grid), dim3(sh.threads), lds, st, M, K, N, sh.rpw,
                        reinterpret_cast<const XT*>(x), b0, inv0, b1, inv1, y);
   } else {
-    auto kern = nvfp4_gemv_kernel<XT, GU, 1, SEG, XF16, Y16>;
-    set_lds_limit(kern, lds);
+    constexpr auto kern = &nvfp4_gemv_kernel<XT, GU, 1, SEG, XF16, Y16>;
+    if (!lds_ok<kern>(lds)) return hipErrorInvalidValue;
     hipLaunchKernelGGL(kern, dim3(sh.grid), dim3(sh.threads), lds, st, M, K, N, sh.rpw,
                        reinterpret_cast<const XT*>(x), b0, inv0, b1, inv1, y);
   }

@@ -553,20 +553,7 @@ __global__ void __launch_bounds__(64 * kItemWaves, 8) nv_lin_grp(int M, int K, i
 #pragma unroll
               for (int r = 0; r < R; ++r) {
                 const u32x2 w = qb[b][r];
-                float pt = 0.f;
-                if constexpr (F16) {
-                  pt = dot16_e2m1_f16(w.x, w.y, x0, x1, pt);
-                  acc[r] = fmaf(pt, e4m3_byte_f32<0>(sb[b][r]), acc[r]);
-                  continue;
-                }
-                pt = dot2_bf16(e2m1x2_bf16<0>(w.x), x0.x, pt);
-                pt = dot2_bf16(e2m1x2_bf16<1>(w.x), x0.y, pt);
-                pt = dot2_bf16(e2m1x2_bf16<2>(w.x), x0.z, pt);
-                pt = dot2_bf16(e2m1x2_bf16<3>(w.x), x0.w, pt);
-                pt = dot2_bf16(e2m1x2_bf16<0>(w.y), x1.x, pt);
-                pt = dot2_bf16(e2m1x2_bf16<1>(w.y), x1.y, pt);
-                pt = dot2_bf16(e2m1x2_bf16<2>(w.y), x1.z, pt);
-                pt = dot2_bf16(e2m1x2_bf16<3>(w.y), x1.w, pt);
+                const float pt = F16 ? dot16_e2m1_f16(w.x, w.y, x0, x1, 0.f) : dot16_e2m1_bf16(w.x, w.y, x0, x1, 0.f);
                 acc[r] = fmaf(pt, e4m3_byte_f32<0>(sb[b][r]), acc[r]);
               }
             }
@@ -633,7 +620,8 @@ __device__ __forceinline__ float dot16_pairs(const uint32_t* d, u32x4 x0, u32x4 
   return acc;
 }
 
-template <bool F16, int MR>
+// ONE: the call has a single activation row (MR = 1; compile-time loop bound).
+template <bool F16, int MR, bool ONE>
 __global__ void __launch_bounds__(64 * kItemWaves) nv_lin_r32(int M, int K, int N, const uint16_t* __restrict__ xa,
                                                            const uint8_t* __restrict__ blk, float inv,
                                                            float* __restrict__ y) {
@@ -659,7 +647,9 @@ __global__ void __launch_bounds__(64 * kItemWaves) nv_lin_r32(int M, int K, int 
   const uint32_t qoff = (uint32_t)(lane >> 1) * 36u + 4u + 16u * (lane & 1);
   const uint32_t soff = (uint32_t)(lane >> 1) * 36u + 2u * (lane & 1);
   const int nslot = U * 4;                             // 16-byte activation pieces per row
-  for (int m0 = 0; m0 < M; m0 += MR) {
+  static_assert(!ONE || MR == 1, "single-row calls take one row per pass");
+  const int Mloop = ONE ? 1 : M;
+  for (int m0 = 0; m0 < Mloop; m0 += MR) {
     if (m0) __syncthreads();                           // the previous pass's LDS reads are done
     for (int i = threadIdx.x; i < MR * NW * RB; i += blockDim.x) (&part[0][0][0])[i] = 0.f;
     // activation rows m0 .. m0+MR-1 (past M: row M-1 again, never stored), piece-major: LDS slot
@@ -719,21 +709,32 @@ __global__ void __launch_bounds__(64 * kItemWaves) nv_lin_r32(int M, int K, int 
       if (u < U) {
         const uint8_t* sp = ringp + stage * kR32Item;
         const uint32_t* wp = reinterpret_cast<const uint32_t*>(sp + qoff);
+        const uint32_t w0 = wp[0], w1 = wp[1], w2 = wp[2], w3 = wp[3];
         const uint32_t sc = *reinterpret_cast<const uint16_t*>(sp + soff);
-        uint32_t d0[8], d1[8];                         // groups 2l and 2l+1, decoded once for all rows
-        e2m1x16_decode<F16>(wp[0], wp[1], d0);
-        e2m1x16_decode<F16>(wp[2], wp[3], d1);
         const float s0 = e4m3_byte_f32<0>(sc), s1 = e4m3_byte_f32<1>(sc);
-#pragma unroll
-        for (int r = 0; r < MR; ++r) {
-          const uint8_t* ar = lds + r * abytes;
+        if constexpr (MR == 1) {                       // decode fused into the dot products
           u32x4 xv[4];
 #pragma unroll
-          for (int qq = 0; qq < 4; ++qq) xv[qq] = *reinterpret_cast<const u32x4*>(ar + ((size_t)qq * U + u) * 16);
-          const float p0 = dot16_pairs<F16>(d0, xv[0], xv[1], 0.f);
-          const float p1 = dot16_pairs<F16>(d1, xv[2], xv[3], 0.f);
-          acc[r] = fmaf(p0, s0, acc[r]);
-          acc[r] = fmaf(p1, s1, acc[r]);
+          for (int qq = 0; qq < 4; ++qq) xv[qq] = *reinterpret_cast<const u32x4*>(lds + ((size_t)qq * U + u) * 16);
+          const float p0 = F16 ? dot16_e2m1_f16(w0, w1, xv[0], xv[1], 0.f) : dot16_e2m1_bf16(w0, w1, xv[0], xv[1], 0.f);
+          const float p1 = F16 ? dot16_e2m1_f16(w2, w3, xv[2], xv[3], 0.f) : dot16_e2m1_bf16(w2, w3, xv[2], xv[3], 0.f);
+          acc[0] = fmaf(p0, s0, acc[0]);
+          acc[0] = fmaf(p1, s1, acc[0]);
+        } else {                                       // groups 2l and 2l+1 decoded once for all rows
+          uint32_t d0[8], d1[8];
+          e2m1x16_decode<F16>(w0, w1, d0);
+          e2m1x16_decode<F16>(w2, w3, d1);
+#pragma unroll
+          for (int r = 0; r < MR; ++r) {
+            const uint8_t* ar = lds + r * abytes;
+            u32x4 xv[4];
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) xv[qq] = *reinterpret_cast<const u32x4*>(ar + ((size_t)qq * U + u) * 16);
+            const float p0 = dot16_pairs<F16>(d0, xv[0], xv[1], 0.f);
+            const float p1 = dot16_pairs<F16>(d1, xv[2], xv[3], 0.f);
+            acc[r] = fmaf(p0, s0, acc[r]);
+            acc[r] = fmaf(p1, s1, acc[r]);
+          }
         }
       }
       wait_lds();                                      // the stage's LDS reads are done before its refill
@@ -758,12 +759,9 @@ __global__ void __launch_bounds__(64 * kItemWaves) nv_lin_r32(int M, int K, int 
   }
 }
 
-template <typename KF>
-bool lds_ok(KF kernel, size_t bytes) {
-  if (bytes > 64 * 1024)
-    return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-                               (int)bytes) == hipSuccess;
-  return true;
+template <auto KERN>
+bool lds_ok(size_t bytes) {
+  return bytes <= 64 * 1024 || raise_lds_limit<KERN>();
 }
 
 constexpr size_t kMaxItemLds = 150 * 1024;
@@ -806,7 +804,7 @@ hipError_t launch_fast_fp8(int M, int K, int N, const void* x, XType xt, const u
   const dim3 grid((N + kItemRows - 1) / kItemRows), block(64 * kItemWaves);
 #define WQ_LAUNCH(T, O)                                                                                     \
   do {                                                                                                      \
-    if (!lds_ok(fp8_lin_items<T, O>, lds)) return hipErrorInvalidValue;                                     \
+    if (!lds_ok<fp8_lin_items<T, O>>(lds)) return hipErrorInvalidValue;                                     \
     hipLaunchKernelGGL((fp8_lin_items<T, O>), grid, block, lds, st, M, K, N, reinterpret_cast<const T*>(x), w0, s0, y); \
   } while (0)
   if (xt == X_F32) {
@@ -850,16 +848,17 @@ hipError_t launch_fast_nvfp4(int M, int K, int N, const void* x, XType xt, const
     const size_t lds = r32_lds_bytes(K, mr);
     const dim3 grid((N + kR32Rows - 1) / kR32Rows), block(64 * kItemWaves);
     const uint16_t* xb = reinterpret_cast<const uint16_t*>(x);
-#define WQ_LAUNCH(F, R)                                                                                      \
+#define WQ_LAUNCH(F, R, O)                                                                                   \
   do {                                                                                                       \
-    if (!lds_ok(nv_lin_r32<F, R>, lds)) return hipErrorInvalidValue;                                         \
-    hipLaunchKernelGGL((nv_lin_r32<F, R>), grid, block, lds, st, M, K, N, xb, b0, inv0, yf);                 \
+    if (!lds_ok<nv_lin_r32<F, R, O>>(lds)) return hipErrorInvalidValue;                                      \
+    hipLaunchKernelGGL((nv_lin_r32<F, R, O>), grid, block, lds, st, M, K, N, xb, b0, inv0, yf);              \
   } while (0)
-#define WQ_MR(F)                      \
-  do {                                \
-    if (mr == 1) WQ_LAUNCH(F, 1);     \
-    else if (mr == 2) WQ_LAUNCH(F, 2); \
-    else WQ_LAUNCH(F, 3);             \
+#define WQ_MR(F)                                  \
+  do {                                            \
+    if (M == 1) WQ_LAUNCH(F, 1, true);            \
+    else if (mr == 1) WQ_LAUNCH(F, 1, false);     \
+    else if (mr == 2) WQ_LAUNCH(F, 2, false);     \
+    else WQ_LAUNCH(F, 3, false);                  \
   } while (0)
     if (xt == X_F16) WQ_MR(true);
     else WQ_MR(false);
@@ -871,7 +870,7 @@ hipError_t launch_fast_nvfp4(int M, int K, int N, const void* x, XType xt, const
   const dim3 grid((N + kItemRows - 1) / kItemRows), block(64 * kItemWaves);
 #define WQ_LAUNCH(T, O, F)                                                                                   \
   do {                                                                                                       \
-    if (!lds_ok(nv_lin_grp<T, O, F>, lds)) return hipErrorInvalidValue;                                      \
+    if (!lds_ok<nv_lin_grp<T, O, F>>(lds)) return hipErrorInvalidValue;                                      \
     hipLaunchKernelGGL((nv_lin_grp<T, O, F>), grid, block, lds, st, M, K, N, reinterpret_cast<const T*>(x), b0, inv0, yf); \
   } while (0)
   if (xt == X_F32) {

@@ -7,7 +7,30 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace wq {
+
+// Raise kernel KERN's dynamic-LDS limit to what the 160 KB of a gfx950 CU leaves beside its static LDS
+// (needed above 64 KB), once per device (the attribute is per kernel and device; devices are tracked as
+// bits, 256 at most).
+template <auto KERN>
+inline bool raise_lds_limit() {
+  static std::atomic<uint64_t> done[4];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 256) return false;
+  const uint64_t bit = (uint64_t)1 << (dev & 63);
+  std::atomic<uint64_t>& word = done[dev >> 6];
+  if (word.load(std::memory_order_acquire) & bit) return true;
+  hipFuncAttributes attr;
+  if (hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(KERN)) != hipSuccess) return false;
+  const int dyn = 160 * 1024 - (int)attr.sharedSizeBytes;   // static LDS of the kernel counts against the CU's
+  if (hipFuncSetAttribute(reinterpret_cast<const void*>(KERN), hipFuncAttributeMaxDynamicSharedMemorySize, dyn) !=
+      hipSuccess)
+    return false;
+  word.fetch_or(bit, std::memory_order_release);
+  return true;
+}
 
 enum XType { X_F32 = 0, X_BF16 = 1, X_F16 = 2 };
 

@@ -832,18 +832,7 @@ template <int FMT, bool GU, int MB, bool BS>
 hipError_t nv_launch(int M, int K, int N, const NvPlan& plan, const uint16_t* a16, const float* rowscale,
                      const uint8_t* w0, const float* cs0, float inv0, const uint8_t* w1, const float* cs1,
                      float inv1, void* out, float* partials, hipStream_t st) {
-  // up to 72 KB of dynamic LDS: raise the per-kernel limit once per device
-  static std::atomic<uint64_t> raised{0};
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  const uint64_t bit = (uint64_t)1 << (dev & 63);
-  if (!(raised.load() & bit)) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(nv_gemm_kernel<FMT, GU, MB, BS>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, g_lds_bytes<FMT>(GU, MB, BS));
-    if (e != hipSuccess) return e;
-    raised.fetch_or(bit);
-  }
+  if (!raise_lds_limit<nv_gemm_kernel<FMT, GU, MB, BS>>()) return hipErrorInvalidValue;   // up to 72 KB
   const int grid = plan.units_grid + (plan.full + 7) / 8 * 8;
   hipLaunchKernelGGL((nv_gemm_kernel<FMT, GU, MB, BS>), dim3(grid), dim3(256), g_lds_bytes<FMT>(GU, MB, BS), st, M, K,
                      N, plan, a16, rowscale, w0, cs0, inv0, w1, cs1, inv1, out, partials);
