@@ -229,7 +229,7 @@ def test_tail_shapes(fmt, M, H, I):
 # ---- hipGraph capture / replay with changing inputs ---------------------------------------------------------
 def test_graph_replay_changing_inputs(nv_big):
     blk, gs, W, dblk = nv_big
-    for M in (1, 256):
+    for M in (1, 8, 256):          # GEMV; 32-row tiles with the block schedule; 128-row tiles with split K
         xs = [synth.nvfp4_x(M, config_id=30 + i)[0] for i in range(3)]
         xin = bf16_dev(xs[0])
         out = torch.empty((M, 5120), dtype=torch.float32, device=DEV)
@@ -246,6 +246,35 @@ def test_graph_replay_changing_inputs(nv_big):
         with torch.cuda.graph(g):
             wq.mlp_nvfp4_run(xin, dblk["gate"], gs["gate"], dblk["up"], gs["up"], dblk["down"], gs["down"],
                              out=out, workspace=ws)
+        for rep in range(2):
+            for i, x in enumerate(xs):
+                xin.copy_(bf16_dev(x))
+                g.replay()
+                torch.cuda.synchronize()
+                assert np.array_equal(host(out).view(np.uint32), eager[i].view(np.uint32)), (M, rep, i)
+
+
+def test_fp8_graph_replay_changing_inputs(fp8_big):
+    # FP8 on both paths inside a captured graph (M=1 GEMV, M=8 and M=256 MFMA with split-K partials in the
+    # workspace): every replay equals the eager call on the same input.
+    d = fp8_big
+    W = fp8_dev(d)
+    for M in (1, 8, 256):
+        r = np.random.default_rng(900 + M)
+        xs = [synth.to_bf16_bits(r.standard_normal((M, 5120)).astype(np.float32)) for _ in range(3)]
+        xin = bf16_dev(xs[0])
+        out = torch.empty((M, 5120), dtype=torch.float32, device=DEV)
+        ws = torch.empty(wq.mlp_workspace_bytes(0, M, 5120, 17408), dtype=torch.uint8, device=DEV)
+        eager = [host(wq.mlp_fp8w_run(bf16_dev(x), *W)) for x in xs]
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            wq.mlp_fp8w_run(xin, *W, out=out, workspace=ws)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            wq.mlp_fp8w_run(xin, *W, out=out, workspace=ws)
         for rep in range(2):
             for i, x in enumerate(xs):
                 xin.copy_(bf16_dev(x))
