@@ -6,6 +6,7 @@ import torch
 import oracle
 import synth
 import weight_quantized_mlp_amd as wq
+from golden import hex_bytes, load as golden
 from gpu_common import DEV, dev, host, same_bits_f32
 
 pytestmark = pytest.mark.gpu
@@ -53,6 +54,16 @@ def test_nvfp4_packer_bytes():
     wp, ws, gs = synth.nvfp4_tensor(96, 640, 3, 7)
     got = host(wq.nvfp4_pack_block64(dev(wp), dev(ws)))
     assert np.array_equal(got, oracle.block64_pack(wp, ws))
+
+
+def test_nvfp4_packer_worked_example():
+    # the page's 36-byte record, written out by hand (tests/golden/nvfp4_block64_record.txt)
+    g = golden("nvfp4_block64_record.txt")
+    codes = (np.arange(64) % 16).astype(np.uint8)[None, :]
+    wp = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    ws = np.frombuffer(hex_bytes(g["example_scales"]), dtype=np.uint8)[None, :].copy()
+    got = host(wq.nvfp4_pack_block64(dev(wp), dev(ws)))
+    assert got.tobytes() == hex_bytes(g["example_record"])
 
 
 @pytest.mark.parametrize("ml", [3, 4])

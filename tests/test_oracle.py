@@ -13,6 +13,7 @@ import torch
 
 import oracle
 import synth
+from golden import hex_bytes, load as golden
 from oracle import codecs, dequant, pack, mlp, moe
 
 pytestmark = pytest.mark.cpu
@@ -135,6 +136,23 @@ def test_awq_dequant_single_rounding_fma():
 
 
 # ---- packers --------------------------------------------------------------------------------------
+def test_block64_record_worked_example():
+    # the page's struct, written out by hand for one 64-weight row (tests/golden/nvfp4_block64_record.txt)
+    g = golden("nvfp4_block64_record.txt")
+    assert int(g["record_bytes"]) == int(g["d_count"]) + int(g["qs_bytes"]) == 36
+    assert g["nibble_order"] == "low_first" and g["example_codes"] == "k mod 16"
+    K = int(g["weights_per_record"])
+    codes = (np.arange(K) % 16).astype(np.uint8)[None, :]
+    wp = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    ws = np.frombuffer(hex_bytes(g["example_scales"]), dtype=np.uint8)[None, :]
+    assert ws.shape[1] == K // int(g["group_size"])
+    blk = pack.block64_pack(wp, ws)
+    assert blk.tobytes() == hex_bytes(g["example_record"])
+    rec = hex_bytes(g["example_record"])
+    d0, q0 = int(g["d_offset"]), int(g["qs_offset"])
+    assert rec[d0:d0 + 4] == hex_bytes(g["example_scales"]) and len(rec[q0:]) == int(g["qs_bytes"])
+
+
 def test_block64_struct_layout():
     N, K = 3, 256
     ws = (np.arange(N * K // 16, dtype=np.uint8).reshape(N, K // 16) + 1)
@@ -182,16 +200,22 @@ def test_awq_bank_round_trip_and_offsets():
             else:   # bias = RN_f16(-z*s)
                 want = (-(z.astype(np.float64)) * s.view(np.float16).astype(np.float64)).astype(np.float16)
                 assert np.array_equal(m2, want.view(np.uint16))
-    # sizes at the routed-expert shape: 3 bytes of metadata per group of 32
-    L13 = pack.awq_bank_layout(320, 2560, 3)
-    L2 = pack.awq_bank_layout(2560, 160, 3)
-    assert L13["expert_bytes"] == 409600 + 320 * 80 * 3
-    assert L2["expert_bytes"] == 204800 + 2560 * 5 * 3
+    # sizes at the routed-expert shape: the metadata bytes per group of 32 that the pull request names
+    # (tests/golden/awq_metadata_layouts.txt), on top of the packed codes
+    g = golden("awq_metadata_layouts.txt")
+    for layout in (3, 4):
+        per_group = int(g[f"layout_{layout}"].split()[0].split("=")[1])
+        assert per_group == layout
+        L13 = pack.awq_bank_layout(320, 2560, layout)
+        L2 = pack.awq_bank_layout(2560, 160, layout)
+        assert L13["expert_bytes"] == 409600 + 320 * 80 * per_group
+        assert L2["expert_bytes"] == 204800 + 2560 * 5 * per_group
 
 
-@pytest.mark.parametrize("kk", [0, 31, 32, 159])
+@pytest.mark.parametrize("kk", [int(v) for v in golden("awq_one_hot_k.txt")["indices"].split()])
 def test_awq_one_hot_boundary_reads(kk):
-    E, N, K = 2, 8, 160
+    # K and the indices the pull request's test plan reads (tests/golden/awq_one_hot_k.txt)
+    E, N, K = 2, 8, int(golden("awq_one_hot_k.txt")["K"])
     codes = np.full((E, N, K), 8, dtype=np.uint8)
     zeros = np.full((E, N, K // 32), 8, dtype=np.uint8)                 # q == z -> exactly 0
     scales = np.full((E, N, K // 32), np.float16(0.25)).view(np.uint16)
