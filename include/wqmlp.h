@@ -227,6 +227,9 @@ int awq_dequant_f16(int64_t E, int64_t N, int64_t K, const void* bank, int meta_
  *   fmt WQ_FMT_FP8W: w = [N, K] E4M3 codes, scale = [N] float32, global_scale ignored
  *   fmt WQ_FMT_NVFP4: w = Block64 [N, K/64], scale = NULL, global_scale as above
  *   y [M, N] float32.  Workspace: qlinear_workspace_bytes.
+ * Shapes: K a positive multiple of 64 for NVFP4 and for the MFMA path, else of
+ * 16; N any positive row count (partial tiles are masked, as in the tail case of
+ * page "Qwen3.8-27B-NVFP4", section "Correctness and precision": 129 x 67 x 320).
  */
 size_t qlinear_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K, int flags);
 int qlinear_run(int fmt, int64_t M, int64_t N, int64_t K, const void* x, int x_dtype,

@@ -158,3 +158,15 @@ def test_packer_and_decoder_validation(L):
     assert L.qlinear_run(2, 1, 64, 64, A, 1, A + 4096, A + 8192, 1.0, None, 0, A + 12288, 0, None) == EINVAL
     assert L.qlinear_run(0, 1, 64, 64, A, 1, A + 4096, None, 1.0, None, 0, A + 12288, 0, None) == EINVAL
     assert L.qlinear_run(1, 128, 64, 64, A, 1, A + 4096, None, 1.0, None, 0, A + 1 << 20, 0, None) == EWORKSPACE
+
+
+def test_qlinear_shape_rules(L):
+    # K carries the alignment (NVFP4 records, MFMA K steps, FP8 16-byte chunks); any N passes the shape
+    # checks (the workspace check after them is what rejects these calls: none is given)
+    assert L.qlinear_run(1, 1, 64, 96, A, 1, A + 4096, None, 1.0, None, 0, A + 12288, 0, None) == EINVAL
+    assert L.qlinear_run(0, 1, 64, 24, A, 1, A + 4096, A + 8192, 1.0, None, 0, A + 12288, 1, None) == EINVAL
+    assert L.qlinear_run(0, 128, 64, 96, A, 1, A + 4096, A + 8192, 1.0, None, 0, A + 12288, 2, None) == EINVAL
+    for fmt, scale in ((1, None), (0, A + 0x100000)):
+        assert L.qlinear_run(fmt, 129, 67, 320, A, 1, A + 0x200000, scale, 1.0, None, 0, A + 0x400000, 0,
+                             None) == EWORKSPACE
+        assert wq.qlinear_workspace_bytes(fmt, 129, 67, 320) > 0

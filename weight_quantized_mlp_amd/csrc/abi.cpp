@@ -380,9 +380,11 @@ int qlinear_run(int fmt, int64_t M, int64_t N, int64_t K, const void* x, int x_d
   if (x_dtype != WQ_F32 && x_dtype != WQ_BF16) return WQ_EINVAL;
   if (M < 0 || M > kMaxDim || N <= 0 || K <= 0 || N > kMaxDim || K > kMaxDim) return WQ_EINVAL;
   const int path = linear_path(fmt, M, N, K, flags);
+  // K runs along the records (NVFP4), the 64-wide MFMA K steps and the 16-byte FP8 chunks; N (output
+  // rows) is free: every kernel clamps its row loads to N-1 and guards its stores
   if (path == WQ_PATH_MFMA || fmt == WQ_FMT_NVFP4) {
-    if (N % 64 || K % 64) return WQ_EINVAL;
-  } else if (N % 16 || K % 16) {
+    if (K % 64) return WQ_EINVAL;
+  } else if (K % 16) {
     return WQ_EINVAL;
   }
   if (path == WQ_PATH_GEMV && !gemv_fits(fmt, K, x_dtype)) return WQ_EINVAL;

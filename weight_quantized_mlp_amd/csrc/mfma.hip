@@ -193,12 +193,14 @@ __global__ void __launch_bounds__(256, 2) mfma_gemm_kernel(int M, int K, int N, 
   const int ncol = n0 + 32 * wave + li;  // this lane's output column / weight row
   const bool wave_on = n0 + 32 * wave < N;
   const int nk = K >> 6;
+  // lanes past the last column (N not a multiple of 32) load row N-1 and store nothing
+  const int wcol = min(ncol, N - 1);
 
   const uint8_t* wrow[NM];
   {
     const size_t rb = FMT == 1 ? (size_t)(K >> 6) * 36 : (size_t)K;
-    wrow[0] = w0 + (size_t)(wave_on ? ncol : 0) * rb;
-    if constexpr (GU) wrow[1] = w1 + (size_t)(wave_on ? ncol : 0) * rb;
+    wrow[0] = w0 + (size_t)(wave_on ? wcol : 0) * rb;
+    if constexpr (GU) wrow[1] = w1 + (size_t)(wave_on ? wcol : 0) * rb;
   }
 
   f32x16 acc[NM][MB];
@@ -314,7 +316,7 @@ __global__ void __launch_bounds__(256, 2) mfma_gemm_kernel(int M, int K, int N, 
     __syncthreads();
   }
 
-  if (!wave_on) return;
+  if (!wave_on || ncol >= N) return;
   float cf[NM];
 #pragma unroll
   for (int t = 0; t < NM; ++t) {
