@@ -793,8 +793,11 @@ __global__ void __launch_bounds__(256, 2) nv_gemm_kernel(int M, int K, int N, Nv
 }
 
 // Epilogue of the split tiles: element (row, col) of split tile i adds its S parts in part order.
-// Workgroup b handles 256 elements of split tile b / (bm / 2) (a tile has bm * 128 elements).
+// A thread handles 4 consecutive columns of one tile row (16-byte partial loads); workgroup b handles 1024
+// elements of split tile b / (bm / 8) (a tile has bm * 128 elements).  Stores are vectors when N is a
+// multiple of 4 and all 4 columns exist, else per column.
 // Column factors as in the GEMM: cs0[n] / cs1[n] (FP8) when cs0 is not null, else inv0 / inv1.
+constexpr int kFinishCols = 4;
 template <bool GU>
 __global__ void __launch_bounds__(256) nv_splitk_finish(int M, int N, NvPlan plan, const float* __restrict__ partials,
                                                        const float* __restrict__ rowscale,
@@ -802,31 +805,57 @@ __global__ void __launch_bounds__(256) nv_splitk_finish(int M, int N, NvPlan pla
                                                        const float* __restrict__ cs1, float inv1,
                                                        void* __restrict__ out) {
   constexpr int NM = GU ? 2 : 1;
-  const int per_tile = plan.bm / 2;                    // workgroups per split tile
-  const int i = (int)blockIdx.x / per_tile;            // split tile index
-  const int e = ((int)blockIdx.x - i * per_tile) * 256 + (int)threadIdx.x;
+  const int per_tile = plan.bm * 128 / (256 * kFinishCols);   // workgroups per split tile
+  const int i = (int)blockIdx.x / per_tile;                   // split tile index
+  const int e = (((int)blockIdx.x - i * per_tile) * 256 + (int)threadIdx.x) * kFinishCols;
   const int pt = plan.bm * 128;
   const int tile = plan.full + i;
   const int tm = tile / plan.ntn, tn = tile - tm * plan.ntn;
   const int m = tm * plan.bm + (e >> 7), n = tn * 128 + (e & 127);
   if (m >= M || n >= N) return;
   const float* p = partials + (size_t)i * plan.S * NM * pt + e;
-  float acc[NM];
+  f32x4 acc[NM];
 #pragma unroll
-  for (int t = 0; t < NM; ++t) acc[t] = p[t * pt];
+  for (int t = 0; t < NM; ++t) acc[t] = *reinterpret_cast<const f32x4*>(p + t * pt);
   for (int s = 1; s < plan.S; ++s)
 #pragma unroll
-    for (int t = 0; t < NM; ++t) acc[t] += p[(size_t)s * NM * pt + t * pt];
+    for (int t = 0; t < NM; ++t) acc[t] += *reinterpret_cast<const f32x4*>(p + (size_t)s * NM * pt + t * pt);
   const float rs = rowscale ? rowscale[m] : 1.0f;
-  const float c0 = cs0 ? cs0[n] : inv0;
+  const bool vec = (N & 3) == 0 && n + kFinishCols <= N;
   if constexpr (GU) {
-    const float c1 = cs0 ? cs1[n] : inv1;
-    const float g = acc[0] * rs * c0;
-    const float u = acc[1] * rs * c1;
-    const _Float16 a = (_Float16)(silu_f32(g) * u);
-    reinterpret_cast<uint16_t*>(out)[(size_t)m * N + n] = __builtin_bit_cast(uint16_t, a);
+    uint16_t a[kFinishCols];
+#pragma unroll
+    for (int j = 0; j < kFinishCols; ++j) {
+      const int nj = min(n + j, N - 1);
+      const float c0 = cs0 ? cs0[nj] : inv0;
+      const float c1 = cs0 ? cs1[nj] : inv1;
+      const float g = acc[0][j] * rs * c0;
+      const float u = acc[1][j] * rs * c1;
+      a[j] = __builtin_bit_cast(uint16_t, (_Float16)(silu_f32(g) * u));
+    }
+    uint16_t* o = reinterpret_cast<uint16_t*>(out) + (size_t)m * N + n;
+    if (vec) {
+      *reinterpret_cast<u32x2*>(o) = u32x2{(uint32_t)a[0] | ((uint32_t)a[1] << 16), (uint32_t)a[2] | ((uint32_t)a[3] << 16)};
+    } else {
+#pragma unroll
+      for (int j = 0; j < kFinishCols; ++j)
+        if (n + j < N) o[j] = a[j];
+    }
   } else {
-    reinterpret_cast<float*>(out)[(size_t)m * N + n] = acc[0] * rs * c0;
+    float y[kFinishCols];
+#pragma unroll
+    for (int j = 0; j < kFinishCols; ++j) {
+      const int nj = min(n + j, N - 1);
+      y[j] = acc[0][j] * rs * (cs0 ? cs0[nj] : inv0);
+    }
+    float* o = reinterpret_cast<float*>(out) + (size_t)m * N + n;
+    if (vec) {
+      *reinterpret_cast<f32x4*>(o) = f32x4{y[0], y[1], y[2], y[3]};
+    } else {
+#pragma unroll
+      for (int j = 0; j < kFinishCols; ++j)
+        if (n + j < N) o[j] = y[j];
+    }
   }
 }
 
@@ -861,7 +890,8 @@ hipError_t nv_dispatch(int M, int K, int N, const uint16_t* a16, const float* ro
       break;
   }
   if (e != hipSuccess || plan.units == 0) return e;
-  hipLaunchKernelGGL((nv_splitk_finish<GU>), dim3((plan.tiles - plan.full) * (plan.bm / 2)), dim3(256), 0, st, M, N,
+  hipLaunchKernelGGL((nv_splitk_finish<GU>), dim3((plan.tiles - plan.full) * (plan.bm * 128 / (256 * kFinishCols))),
+                     dim3(256), 0, st, M, N,
                      plan, partials, rowscale, cs0, inv0, cs1, inv1, out);
   return hipGetLastError();
 }
