@@ -17,6 +17,8 @@ rotating weights, timed the same way.
 Extras measured the same way: NVFP4 decode, NVFP4 prefill at M=512 and 8192
 (MFMA utilisation), both formats at a short batch (M=8) and FP8 at M=512 on the
 MFMA path, and the AWQ routed-expert step (hot and rotating experts).
+Opt-in extra "dense_f16": torch's own float16 matmul on the same prefill shapes
+(unquantized weights; context for the MFMA fraction, not part of the path).
 The CPU oracle is timed on the host on a bounded sample as a baseline.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--extras all|none|a,b]
@@ -249,6 +251,35 @@ def awq_run(torch, wq, synth, K):
     return dict(hot_s=res["hot"], rot_s=res["rotating"], step_bytes=step_bytes, K=K)
 
 
+def dense_f16_ref(torch, M, K):
+    """torch float16 matmuls of the prefill shapes with unquantized weights: [M,H] x [2I,H]^T (gate and up
+    as one matrix) and [M,I] x [H,I]^T; context for the MFMA fraction of the quantized GEMMs."""
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(7)
+    x = torch.randn(M, H, device=dev, dtype=torch.float16, generator=g)
+    wgu = torch.randn(2 * I, H, device=dev, dtype=torch.float16, generator=g) * 0.02
+    wd = torch.randn(H, I, device=dev, dtype=torch.float16, generator=g) * 0.02
+    a = torch.randn(M, I, device=dev, dtype=torch.float16, generator=g)
+    y1 = torch.empty(M, 2 * I, device=dev, dtype=torch.float16)
+    y2 = torch.empty(M, H, device=dev, dtype=torch.float16)
+
+    def step():
+        torch.matmul(x, wgu.t(), out=y1)
+        torch.matmul(a, wd.t(), out=y2)
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(K):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / K
+    del x, wgu, wd, a, y1, y2
+    return ms
+
+
 def cpu_baseline(oracle, d, budget_s):
     """The oracle as it stands, on this host, on the headline workload (full calls)."""
     import numpy as np
@@ -408,6 +439,13 @@ def main():
                 down_mfma_frac=round(2.0 * M * H * I / (n["dn_ms"] / 1e3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4))
             log(key, extras[key])
         del blk
+    if "dense_f16" in want:
+        for M, steps in ((512, 100), (8192, 12)):
+            ms = dense_f16_ref(torch, M, steps)
+            tfl = 2.0 * M * 3 * H * I / (ms / 1e3) / 1e12
+            extras[f"torch_f16_matmul_{M}"] = dict(ms_per_step=round(ms, 4), TFLOPs=round(tfl, 1),
+                                                   mfma_frac_f16_peak=round(tfl / MFMA_F16_PEAK_TFLOPS, 4))
+            log(f"torch f16 matmul M={M}", extras[f"torch_f16_matmul_{M}"])
     if "awq" in want:
         a = awq_run(torch, wq, synth, 480)
         extras["awq_moe_m1"] = dict(
