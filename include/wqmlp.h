@@ -72,6 +72,10 @@ enum { WQ_STAGE_GATEUP_ONLY = 4, WQ_STAGE_DOWN_ONLY = 8 };
 #define WQ_NARROW_MIN_WEIGHT_BYTES (16u << 20)
 /* largest top-k the routed-expert step accepts */
 #define WQ_MOE_MAX_TOPK 16
+/* largest value of every dimension (M, H, I, N, K, E); larger ones are WQ_EINVAL.  The kernels that
+ * move data by global->LDS copies address it with 32-bit offsets inside one 128-row activation tile or
+ * one weight row (64-bit bases), which this bound keeps below 2^31 bytes. */
+#define WQ_MAX_DIM (1 << 23)
 
 /* ABI version of the loaded library (WQ_ABI_VERSION). */
 int wq_abi_version(void);
@@ -86,8 +90,8 @@ int wq_last_hip_error(void);
  * invalid arguments or M == 0.
  *   GEMV path: act [M, I], float32 (FP8) or float16 (NVFP4).
  *   MFMA path: x as float16 [M, H] (row-scaled), per-row scales float32 [M],
- *              act float16 [M, I], then (NVFP4) float32 split-K partial
- *              tiles of at most 64 MiB; each region 256-byte aligned.
+ *              act float16 [M, I], then float32 split-K partial tiles of
+ *              at most 64 MiB; each region 256-byte aligned.
  *              The size is a function of the shape alone.
  */
 size_t mlp_workspace_bytes(int fmt, int64_t M, int64_t H, int64_t I, int flags);

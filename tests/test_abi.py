@@ -54,7 +54,7 @@ def test_workspace_queries(L):
     n = wq.mlp_workspace_bytes(1, 512, 5120, 17408)
     assert n >= 512 * 5120 * 2 + 512 * 4 + 512 * 17408 * 2
     assert wq.mlp_workspace_bytes(1, 4, 5120, 17408, "gemv") == 4 * 17408 * 2   # NVFP4 act: float16
-    # MFMA path: x16, row scales, act16, then (NVFP4) split-K partial tiles of at most 64 MiB
+    # MFMA path: x16, row scales, act16, then split-K partial tiles of at most 64 MiB
     base = 4 * 5120 * 2 + 256 + 4 * 17408 * 2
     for fmt in (0, 1):                                   # + the split-K partial tiles
         assert base < wq.mlp_workspace_bytes(fmt, 4, 5120, 17408, "mfma") <= base + (64 << 20)
@@ -72,6 +72,11 @@ def test_workspace_queries(L):
     assert wq.mlp_workspace_bytes(0, 0, 64, 64) == 0
     assert wq.qlinear_workspace_bytes(1, 4, 64, 64) == 0
     assert wq.qlinear_workspace_bytes(1, 128, 64, 64) > 0
+    # every dimension is capped at WQ_MAX_DIM = 2^23
+    assert wq.mlp_workspace_bytes(1, 1 << 23, 64, 64) > 0
+    assert wq.mlp_workspace_bytes(1, (1 << 23) + 1, 64, 64) == 0
+    assert wq.mlp_workspace_bytes(0, 1, 64, (1 << 23) + 64) == 0
+    assert wq.qlinear_workspace_bytes(1, (1 << 23) + 1, 64, 64) == 0
 
 
 @pytest.mark.parametrize("E,N,K", [(512, 320, 2560), (512, 2560, 160), (3, 64, 96)])

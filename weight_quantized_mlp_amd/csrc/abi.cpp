@@ -108,7 +108,7 @@ bool gemv_fits(int fmt, int64_t K, int dt) {
   return per_row <= 160 * 1024;
 }
 
-constexpr int64_t kMaxDim = (int64_t)1 << 30;
+constexpr int64_t kMaxDim = WQ_MAX_DIM;
 
 size_t wbytes(int fmt, int64_t N, int64_t K) {
   return fmt == WQ_FMT_FP8W ? (size_t)N * (size_t)K : (size_t)N * (size_t)(K / 64) * 36;

@@ -669,9 +669,10 @@ __global__ void __launch_bounds__(64 * kItemWaves) nv_lin_r32(int M, int K, int 
     int lg = wv / T, lt = wv - (wv / T) * T, lk = 0;
     auto issue = [&](int stage) {
       const uint32_t st = ring + stage * kR32Item;
-      const uint32_t base = (uint32_t)min(rowof(lg), N - 1) * rb, off = 1152u * lt;
-      lds_copy16(base + min(off + q0, rb - 16u), blk, __builtin_amdgcn_readfirstlane(st));
-      if (lane < 8) lds_copy16(base + min(off + q1, rb - 16u), blk, __builtin_amdgcn_readfirstlane(st + 1024));
+      const uint8_t* rowp = blk + (size_t)min(rowof(lg), N - 1) * rb;   // 64-bit row base, 32-bit offsets in the row
+      const uint32_t off = 1152u * lt;
+      lds_copy16(min(off + q0, rb - 16u), rowp, __builtin_amdgcn_readfirstlane(st));
+      if (lane < 8) lds_copy16(min(off + q1, rb - 16u), rowp, __builtin_amdgcn_readfirstlane(st + 1024));
       ++lk;
       if (lk < nk) {                                   // past the wave's last item: repeat it (never used)
         lt += NW;

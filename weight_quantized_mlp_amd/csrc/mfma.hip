@@ -489,17 +489,23 @@ __global__ void __launch_bounds__(256, 2) nv_gemm_kernel(int M, int K, int N, Nv
   const uint8_t* wbuf = lds + AS * kNvAStage + wave * g_wave_wbytes<FMT>(GU);
 
   // Activation chunk p = tid + 256 i: tile row p >> 3, LDS chunk p & 7, global chunk (p & 7) ^ (row & 7).
+  // Offsets are relative to the tile's first row (64-bit base), so they stay below 32 * MB * K * 2 bytes.
+  const uint8_t* a_tile = reinterpret_cast<const uint8_t*>(a16) + (size_t)m0 * K * 2;
   uint32_t aoff[MB];
 #pragma unroll
   for (int i = 0; i < MB; ++i) {
     const int p = tid + 256 * i, row = p >> 3, c = p & 7;
-    aoff[i] = (uint32_t)min(m0 + row, M - 1) * (uint32_t)K * 2u + (uint32_t)((c ^ (row & 7)) * 16);
+    aoff[i] = (uint32_t)(min(m0 + row, M - 1) - m0) * (uint32_t)K * 2u + (uint32_t)((c ^ (row & 7)) * 16);
   }
   // Weight copy j = CPM t + i of matrix t writes LDS slot s = 64 i + lane of the matrix's block buffer
   // (wbuf + MBYTES t).  NVFP4: column c = s / 9, chunk q = s % 9 of the column's 144-byte block (slots
   // 288..319 re-read chunks of slots 0..31), the column's block at 144 c.  FP8: column c = s / 8, slot
   // position p = s % 8 holds chunk p ^ ((c / 2) % 8) of the column's 128-byte block (a swizzle that keeps
   // the 16-byte fragment reads of 16 consecutive columns on distinct banks), the column's block at 128 c.
+  // Offsets are relative to the wave's first column row (64-bit bases), so they stay below 32 rows.
+  const int nw0 = min(n0 + 32 * wave, N - 1);
+  const uint8_t* wbase0 = w0 + (size_t)nw0 * rb;
+  const uint8_t* wbase1 = GU ? w1 + (size_t)nw0 * rb : wbase0;
   uint32_t woff[NW];
 #pragma unroll
   for (int j = 0; j < NW; ++j) {
@@ -513,11 +519,11 @@ __global__ void __launch_bounds__(256, 2) nv_gemm_kernel(int M, int K, int N, Nv
       c = s >> 3;
       q = (s & 7) ^ ((c >> 1) & 7);
     }
-    woff[j] = (uint32_t)min(n0 + 32 * wave + c, N - 1) * rb + 16u * (uint32_t)q;
+    woff[j] = (uint32_t)(min(n0 + 32 * wave + c, N - 1) - nw0) * rb + 16u * (uint32_t)q;
   }
   auto copy_a = [&](int kt, int stage) {
     kt = min(kt, nk - 1);
-    const uint8_t* base = reinterpret_cast<const uint8_t*>(a16) + (size_t)kt * 128;
+    const uint8_t* base = a_tile + (size_t)kt * 128;
     const uint32_t sb = lds0 + stage * kNvAStage;
 #pragma unroll
     for (int i = 0; i < MB; ++i) lds_copy16(aoff[i], base, __builtin_amdgcn_readfirstlane(sb + (256 * i + 64 * wave) * 16));
@@ -531,7 +537,7 @@ __global__ void __launch_bounds__(256, 2) nv_gemm_kernel(int M, int K, int N, Nv
     const uint32_t boff = (rtail && blk == nblk - 1) ? rb - (uint32_t)CB : (uint32_t)blk * CB;
 #pragma unroll
     for (int j = 0; j < NW; ++j)
-      lds_copy16(woff[j] + boff, j < CPM ? w0 : w1, __builtin_amdgcn_readfirstlane(wlds + 1024 * j));
+      lds_copy16(woff[j] + boff, j < CPM ? wbase0 : wbase1, __builtin_amdgcn_readfirstlane(wlds + 1024 * j));
   };
 
   f32x16 acc[NM][MB];
