@@ -76,6 +76,9 @@ enum { WQ_STAGE_GATEUP_ONLY = 4, WQ_STAGE_DOWN_ONLY = 8 };
  * move data by global->LDS copies address it with 32-bit offsets inside one 128-row activation tile or
  * one weight row (64-bit bases), which this bound keeps below 2^31 bytes. */
 #define WQ_MAX_DIM (1 << 23)
+/* largest element count of any activation or output matrix: M x max(H, I) for the MLP, M x max(N, K)
+ * for the single linear (2^36 float32 elements are 256 GiB); larger calls are WQ_EINVAL. */
+#define WQ_MAX_ELEMS ((int64_t)1 << 36)
 
 /* ABI version of the loaded library (WQ_ABI_VERSION). */
 int wq_abi_version(void);

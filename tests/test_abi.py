@@ -77,6 +77,10 @@ def test_workspace_queries(L):
     assert wq.mlp_workspace_bytes(1, (1 << 23) + 1, 64, 64) == 0
     assert wq.mlp_workspace_bytes(0, 1, 64, (1 << 23) + 64) == 0
     assert wq.qlinear_workspace_bytes(1, (1 << 23) + 1, 64, 64) == 0
+    # ... and every activation or output matrix at 2^36 elements
+    assert wq.mlp_workspace_bytes(1, 1 << 23, 1 << 13, 64) > 0
+    assert wq.mlp_workspace_bytes(1, 1 << 23, 64, (1 << 13) + 64) == 0
+    assert wq.qlinear_workspace_bytes(1, 1 << 23, (1 << 13) + 1, 64) == 0
 
 
 @pytest.mark.parametrize("E,N,K", [(512, 320, 2560), (512, 2560, 160), (3, 64, 96)])

@@ -109,6 +109,9 @@ bool gemv_fits(int fmt, int64_t K, int dt) {
 }
 
 constexpr int64_t kMaxDim = WQ_MAX_DIM;
+// rows x columns of any activation or output matrix (keeps tile and grid counts in int)
+constexpr int64_t kMaxElems = WQ_MAX_ELEMS;
+bool elems_ok(int64_t M, int64_t a, int64_t b) { return M * std::max(a, b) <= kMaxElems; }
 
 size_t wbytes(int fmt, int64_t N, int64_t K) {
   return fmt == WQ_FMT_FP8W ? (size_t)N * (size_t)K : (size_t)N * (size_t)(K / 64) * 36;
@@ -146,7 +149,7 @@ size_t act_gemv_bytes(int fmt) { return fmt == WQ_FMT_NVFP4 ? 2 : 4; }
 
 // Workspace of the two-layer MLP; 0 means "invalid".
 size_t mlp_ws(int fmt, int64_t M, int64_t H, int64_t I, int flags) {
-  if (M <= 0 || H <= 0 || I <= 0 || M > kMaxDim || H > kMaxDim || I > kMaxDim) return 0;
+  if (M <= 0 || H <= 0 || I <= 0 || M > kMaxDim || H > kMaxDim || I > kMaxDim || !elems_ok(M, H, I)) return 0;
   if (mlp_path(fmt, M, H, I, flags) == WQ_PATH_GEMV) return align256((size_t)M * I * act_gemv_bytes(fmt));
   return align256((size_t)M * H * 2) + align256((size_t)M * 4) + align256((size_t)M * I * 2) +
          align256(mlp_partials(fmt, M, H, I));
@@ -173,7 +176,7 @@ int mlp_run(int fmt, int64_t M, int64_t H, int64_t I, const void* x, int x_dtype
   const bool do_gu = stage != WQ_STAGE_DOWN_ONLY, do_down = stage != WQ_STAGE_GATEUP_ONLY;
   if (x_dtype != WQ_F32 && x_dtype != WQ_BF16) return WQ_EINVAL;
   if (M < 0 || M > kMaxDim) return WQ_EINVAL;
-  if (H <= 0 || I <= 0 || H > kMaxDim || I > kMaxDim) return WQ_EINVAL;
+  if (H <= 0 || I <= 0 || H > kMaxDim || I > kMaxDim || !elems_ok(M, H, I)) return WQ_EINVAL;
   const int path = mlp_path(fmt, M, H, I, flags);
   if (!shape_ok(fmt, path, H, I, x_dtype)) return WQ_EINVAL;
   if (any_null({x, wg, wu, wd, out})) return WQ_EINVAL;
@@ -366,7 +369,7 @@ int awq_dequant_f16(int64_t E, int64_t N, int64_t K, const void* bank, int meta_
 
 size_t qlinear_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K, int flags) {
   if ((fmt != WQ_FMT_FP8W && fmt != WQ_FMT_NVFP4) || flags < WQ_PATH_AUTO || flags > WQ_PATH_MFMA) return 0;
-  if (M <= 0 || N <= 0 || K <= 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return 0;
+  if (M <= 0 || N <= 0 || K <= 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim || !elems_ok(M, N, K)) return 0;
   if (linear_path(fmt, M, N, K, flags) == WQ_PATH_GEMV) return 0;
   return align256((size_t)M * K * 2) + align256((size_t)M * 4) +
          align256(wq::mfma_partial_bytes(fmt == WQ_FMT_NVFP4 ? 1 : 0, (int)M, (int)K, (int)N, false));
@@ -378,7 +381,7 @@ int qlinear_run(int fmt, int64_t M, int64_t N, int64_t K, const void* x, int x_d
   if (fmt != WQ_FMT_FP8W && fmt != WQ_FMT_NVFP4) return WQ_EINVAL;
   if (flags < WQ_PATH_AUTO || flags > WQ_PATH_MFMA) return WQ_EINVAL;
   if (x_dtype != WQ_F32 && x_dtype != WQ_BF16) return WQ_EINVAL;
-  if (M < 0 || M > kMaxDim || N <= 0 || K <= 0 || N > kMaxDim || K > kMaxDim) return WQ_EINVAL;
+  if (M < 0 || M > kMaxDim || N <= 0 || K <= 0 || N > kMaxDim || K > kMaxDim || !elems_ok(M, N, K)) return WQ_EINVAL;
   const int path = linear_path(fmt, M, N, K, flags);
   // K runs along the records (NVFP4), the 64-wide MFMA K steps and the 16-byte FP8 chunks; N (output
   // rows) is free: every kernel clamps its row loads to N-1 and guards its stores
