@@ -92,7 +92,8 @@ int wq_last_hip_error(void);
  * shape and path.  fmt: WQ_FMT_*; flags as for the run call.  Returns 0 for
  * invalid arguments or M == 0.
  *   GEMV path: act [M, I], float32 (FP8) or float16 (NVFP4).
- *   MFMA path: x as float16 [M, H] (row-scaled), per-row scales float32 [M],
+ *   MFMA path: x as float16 [M, H] (row-scaled; unused for FP8 with bf16 x),
+ *              per-row scales float32 [M],
  *              act float16 [M, I], then float32 split-K partial tiles of
  *              at most 64 MiB; each region 256-byte aligned.
  *              The size is a function of the shape alone.
@@ -116,6 +117,11 @@ size_t mlp_workspace_bytes(int fmt, int64_t M, int64_t H, int64_t I, int flags);
  * that does not depend on M, so results are bitwise reproducible and row m of
  * an M-row call equals a 1-row call on row m.  The MFMA path is reproducible
  * for a given shape; its split-K plan, and so its rounding, depends on M.
+ * MFMA path numerics: with bf16 x the gate/up GEMM runs bf16 MFMAs on x as
+ * given; float32 x is scaled per row by a power of two and rounded to float16
+ * (bf16-representable values give the same bits either way); E4M3 codes decode
+ * exactly; act = silu(g) * u is rounded to float16 for the down GEMM, so |act|
+ * must stay below 65504.
  */
 int mlp_fp8w_run(int64_t M, int64_t H, int64_t I, const void* x, int x_dtype,
                  const uint8_t* w_gate, const float* s_gate,

@@ -84,6 +84,23 @@ def test_fp8_prefill_M512_reproducible_sampled_rows(fp8_big):
     gate(y1[rows], ref, what="fp8 M=512 sampled rows (mfma)")
 
 
+@pytest.mark.parametrize("M", [8, 200])
+def test_fp8_mfma_bf16_x_same_bits_as_f32_x(fp8_big, M):
+    # bf16 x takes bf16 MFMAs on x as given; float32 x holding the same values is row-scaled by a power of
+    # two to float16 first.  Every product is exact in both forms and the scaling is exact, so the MLP and
+    # the single linear give the same bits.
+    d = fp8_big
+    xb = synth.to_bf16_bits(np.random.default_rng(M + 77).standard_normal((M, 5120)).astype(np.float32))
+    W = fp8_dev(d)
+    yb = host(wq.mlp_fp8w_run(bf16_dev(xb), *W, path="mfma"))
+    yf = host(wq.mlp_fp8w_run(dev(oracle.bf16_bits_to_f64(xb).astype(np.float32)), *W, path="mfma"))
+    assert np.array_equal(yb.view(np.uint32), yf.view(np.uint32))
+    lb = host(wq.qlinear_run(wq.WQ_FMT_FP8W, bf16_dev(xb), W[0], W[1], path="mfma"))
+    lf = host(wq.qlinear_run(wq.WQ_FMT_FP8W, dev(oracle.bf16_bits_to_f64(xb).astype(np.float32)), W[0], W[1],
+                             path="mfma"))
+    assert np.array_equal(lb.view(np.uint32), lf.view(np.uint32))
+
+
 # ---- NVFP4 (H=5120, I=17408) ----------------------------------------------------------------------
 @pytest.fixture(scope="module")
 def nv_big():

@@ -225,14 +225,20 @@ int mlp_run(int fmt, int64_t M, int64_t H, int64_t I, const void* x, int x_dtype
                         : nullptr;
   const int f = fmt == WQ_FMT_NVFP4 ? 1 : 0;
   if (do_gu) {
-    rc = launched(wq::launch_rowscale_f16(m, h, x, xt, x16, rs, st));
-    if (rc == WQ_OK)
-      rc = launched(wq::launch_mfma_gateup(f, m, h, i, x16, rs, wg, sg, f ? 1.0f / gg : 0.f, wu, su,
-                                           f ? 1.0f / gu : 0.f, act16, partials, st));
+    // FP8 with bf16 x: bf16 MFMAs on x as given; otherwise x is row-scaled to float16 first
+    if (xt == wq::X_BF16 && wq::mfma_bf16_ok(f, h)) {
+      rc = launched(wq::launch_mfma_gateup(f, m, h, i, reinterpret_cast<const uint16_t*>(x), nullptr, wg, sg, 0.f,
+                                           wu, su, 0.f, act16, partials, true, st));
+    } else {
+      rc = launched(wq::launch_rowscale_f16(m, h, x, xt, x16, rs, st));
+      if (rc == WQ_OK)
+        rc = launched(wq::launch_mfma_gateup(f, m, h, i, x16, rs, wg, sg, f ? 1.0f / gg : 0.f, wu, su,
+                                             f ? 1.0f / gu : 0.f, act16, partials, false, st));
+    }
   }
   if (rc == WQ_OK && do_down)
     rc = launched(wq::launch_mfma_linear(f, m, i, h, act16, nullptr, wd, sd, f ? 1.0f / gd : 0.f, out, partials,
-                                         st));
+                                         false, st));
   return rc;
 }
 
@@ -419,9 +425,12 @@ int qlinear_run(int fmt, int64_t M, int64_t N, int64_t K, const void* x, int x_d
   float* partials = wq::mfma_partial_bytes(f, (int)M, (int)K, (int)N, false)
                         ? reinterpret_cast<float*>(base + align256((size_t)M * K * 2) + align256((size_t)M * 4))
                         : nullptr;
+  if (xt == wq::X_BF16 && wq::mfma_bf16_ok(f, (int)K))   // FP8 with bf16 x: bf16 MFMAs on x as given
+    return launched(wq::launch_mfma_linear(f, (int)M, (int)K, (int)N, reinterpret_cast<const uint16_t*>(x), nullptr,
+                                           w, scale, inv, y, partials, true, st));
   rc = launched(wq::launch_rowscale_f16((int)M, (int)K, x, xt, x16, rs, st));
   if (rc == WQ_OK)
-    rc = launched(wq::launch_mfma_linear(f, (int)M, (int)K, (int)N, x16, rs, w, scale, inv, y, partials, st));
+    rc = launched(wq::launch_mfma_linear(f, (int)M, (int)K, (int)N, x16, rs, w, scale, inv, y, partials, false, st));
   return rc;
 }
 

@@ -63,14 +63,17 @@ hipError_t launch_rowscale_f16(int M, int K, const void* x, XType xt, uint16_t* 
 // gate+up: act16[m,n] = f16(silu(g) * u) with g = rowscale[m]*colscale(n)*acc.
 // partials: float32 scratch of mfma_partial_bytes(fmt, M, K, N, gu) bytes (NULL allowed when that is 0);
 // the NVFP4 GEMM splits the tiles of an underfilled last round along K and finishes them from there.
+// abf: the activations are bfloat16 bits as given (rowscale must be null) and the GEMM runs bf16 MFMAs;
+// only where mfma_bf16_ok(fmt, K) (FP8 weights, K >= 128), else hipErrorInvalidValue.
 size_t mfma_partial_bytes(int fmt, int M, int K, int N, bool gu);
+bool mfma_bf16_ok(int fmt, int K);
 hipError_t launch_mfma_gateup(int fmt, int M, int K, int N, const uint16_t* x16, const float* rowscale,
                               const uint8_t* w0, const float* cs0, float inv0,
                               const uint8_t* w1, const float* cs1, float inv1,
-                              uint16_t* act16, float* partials, hipStream_t st);
+                              uint16_t* act16, float* partials, bool abf, hipStream_t st);
 // single matrix: y[m,n] = rowscale[m] (1 if null) * colscale(n) * sum_k a16[m,k] dq(w[n,k]).
 hipError_t launch_mfma_linear(int fmt, int M, int K, int N, const uint16_t* a16, const float* rowscale,
-                              const uint8_t* w, const float* cs, float inv, float* y, float* partials,
+                              const uint8_t* w, const float* cs, float inv, float* y, float* partials, bool abf,
                               hipStream_t st);
 
 // ---- AWQ routed-expert single-token step ------------------------------------------------------

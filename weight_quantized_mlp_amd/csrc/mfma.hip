@@ -57,6 +57,7 @@ namespace wq {
 namespace {
 
 constexpr int kLdsRow = 144;  // 64 f16 + 16 bytes padding
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ u32x4 ld16(const uint8_t* p) {
   u32x4 v;
@@ -435,8 +436,9 @@ inline size_t nv_partial_bytes(const NvPlan& p, bool gu) {
 }
 
 // FMT 1: NVFP4 Block64 weights, column factor inv0 / inv1.  FMT 0: FP8 E4M3 codes [N][K], column scales
-// cs0[n] / cs1[n].
-template <int FMT, bool GU, int MB, bool BS>
+// cs0[n] / cs1[n].  ABF (FMT 0 only): a16 holds bfloat16 activations as given (no row scale) and the
+// MFMAs run on bf16 operands (E4M3 codes decode to bf16 exactly); otherwise both operands are f16.
+template <int FMT, bool GU, int MB, bool BS, bool ABF>
 __global__ void __launch_bounds__(256, 2) nv_gemm_kernel(int M, int K, int N, NvPlan plan,
                                                         const uint16_t* __restrict__ a16,
                                                         const float* __restrict__ rowscale,
@@ -444,7 +446,9 @@ __global__ void __launch_bounds__(256, 2) nv_gemm_kernel(int M, int K, int N, Nv
                                                         float inv0, const uint8_t* __restrict__ w1,
                                                         const float* __restrict__ cs1, float inv1,
                                                         void* __restrict__ out, float* __restrict__ partials) {
+  static_assert(!ABF || FMT == 0, "bf16 operands: FP8 weights only");
   using Geo = WGeo<FMT>;
+  using AFrag = std::conditional_t<ABF, bf16x8, f16x8>;   // 8 activations (or weights) of one MFMA operand
   constexpr int KSB = Geo::KSB, CB = Geo::CB, CPM = Geo::CPM, MBYTES = Geo::MBYTES;
   constexpr int NM = GU ? 2 : 1;
   constexpr int kNvAStage = nv_astage(MB);
@@ -608,18 +612,26 @@ __global__ void __launch_bounds__(256, 2) nv_gemm_kernel(int M, int K, int N, Nv
       }
     }
   };
-  auto read_a = [&](int stage, int s, f16x8* af) {
+  auto read_a = [&](int stage, int s, AFrag* af) {
     const uint8_t* ast = lds + stage * kNvAStage;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
-      af[mb] = *reinterpret_cast<const f16x8*>(ast + (32 * mb + li) * 128 + (((4 * h + s) ^ (li & 7)) * 16));
+      af[mb] = *reinterpret_cast<const AFrag*>(ast + (32 * mb + li) * 128 + (((4 * h + s) ^ (li & 7)) * 16));
   };
   // decode sub-step s of step J into exact f16 (NVFP4: E2M1 x E4M3 group scale; FP8: the E4M3 codes)
   // and run its MFMAs
-  auto mfmas = [&](const WBlock* wb, int J, int s, const f16x8* af) {
-    f16x8 bfr[NM];
+  auto mfmas = [&](const WBlock* wb, int J, int s, const AFrag* af) {
+    AFrag bfr[NM];
 #pragma unroll
     for (int t = 0; t < NM; ++t) {
+      if constexpr (ABF) {                                             // FP8 codes -> exact bf16
+        const u32x4 ch = wb[t].c[J][s >> 1];
+        const uint32_t wa = (s & 1) ? ch.z : ch.x, wb2 = (s & 1) ? ch.w : ch.y;
+        const bf16x2 q0 = e4m3x2_bf16<false>(wa), q1 = e4m3x2_bf16<true>(wa);
+        const bf16x2 q2 = e4m3x2_bf16<false>(wb2), q3 = e4m3x2_bf16<true>(wb2);
+        bfr[t] = bf16x8{q0.x, q0.y, q1.x, q1.y, q2.x, q2.y, q3.x, q3.y};
+        continue;
+      }
       f16x2 p0, p1, p2, p3;
       if constexpr (FMT == 1) {
         const f16x2 dsc = e4m3x2_f16<false>(wb[t].d[J] >> (16 * h));   // groups 2h, 2h+1
@@ -638,13 +650,15 @@ __global__ void __launch_bounds__(256, 2) nv_gemm_kernel(int M, int K, int N, Nv
         p2 = e4m3x2_f16<false>(wb2);
         p3 = e4m3x2_f16<true>(wb2);
       }
-      bfr[t] = f16x8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+      if constexpr (!ABF) bfr[t] = AFrag{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
     }
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int t = 0; t < NM; ++t)
-        acc[t][mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[mb], bfr[t], acc[t][mb], 0, 0, 0);
+      for (int t = 0; t < NM; ++t) {
+        if constexpr (ABF) acc[t][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], bfr[t], acc[t][mb], 0, 0, 0);
+        else acc[t][mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[mb], bfr[t], acc[t][mb], 0, 0, 0);
+      }
 #pragma unroll
     for (int i = 0; i < MB * NM; ++i) {      // one MFMA, one fragment read, two ALU ops at a time
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -654,7 +668,7 @@ __global__ void __launch_bounds__(256, 2) nv_gemm_kernel(int M, int K, int N, Nv
   };
 
   WBlock wb[NM];
-  f16x8 af0[MB], af1[MB];
+  AFrag af0[MB], af1[MB];
   if constexpr (!BS) {
     // Stepped schedule (128-row tiles: a K step's MFMAs are long enough to cover an activation copy).
     // Prologue: weight block 0, activation steps 0 and 1; wait for block 0 and step 0 (step 1 may fly),
@@ -869,18 +883,18 @@ __global__ void __launch_bounds__(256) nv_splitk_finish(int M, int N, NvPlan pla
   }
 }
 
-template <int FMT, bool GU, int MB, bool BS>
+template <int FMT, bool GU, int MB, bool BS, bool ABF>
 hipError_t nv_launch(int M, int K, int N, const NvPlan& plan, const uint16_t* a16, const float* rowscale,
                      const uint8_t* w0, const float* cs0, float inv0, const uint8_t* w1, const float* cs1,
                      float inv1, void* out, float* partials, hipStream_t st) {
-  if (!raise_lds_limit<nv_gemm_kernel<FMT, GU, MB, BS>>()) return hipErrorInvalidValue;   // up to 72 KB
+  if (!raise_lds_limit<nv_gemm_kernel<FMT, GU, MB, BS, ABF>>()) return hipErrorInvalidValue;   // up to 72 KB
   const int grid = plan.units_grid + (plan.full + 7) / 8 * 8;
-  hipLaunchKernelGGL((nv_gemm_kernel<FMT, GU, MB, BS>), dim3(grid), dim3(256), g_lds_bytes<FMT>(GU, MB, BS), st, M, K,
-                     N, plan, a16, rowscale, w0, cs0, inv0, w1, cs1, inv1, out, partials);
+  hipLaunchKernelGGL((nv_gemm_kernel<FMT, GU, MB, BS, ABF>), dim3(grid), dim3(256), g_lds_bytes<FMT>(GU, MB, BS), st, M,
+                     K, N, plan, a16, rowscale, w0, cs0, inv0, w1, cs1, inv1, out, partials);
   return hipGetLastError();
 }
 
-template <int FMT, bool GU>
+template <int FMT, bool GU, bool ABF>
 hipError_t nv_dispatch(int M, int K, int N, const uint16_t* a16, const float* rowscale, const uint8_t* w0,
                        const float* cs0, float inv0, const uint8_t* w1, const float* cs1, float inv1, void* out,
                        float* partials, hipStream_t st) {
@@ -890,13 +904,13 @@ hipError_t nv_dispatch(int M, int K, int N, const uint16_t* a16, const float* ro
   hipError_t e;
   switch (plan.bm) {
     case 32:
-      e = nv_launch<FMT, GU, 1, true>(M, K, N, plan, a16, rowscale, w0, cs0, inv0, w1, cs1, inv1, out, partials, st);
+      e = nv_launch<FMT, GU, 1, true, ABF>(M, K, N, plan, a16, rowscale, w0, cs0, inv0, w1, cs1, inv1, out, partials, st);
       break;
     case 64:
-      e = nv_launch<FMT, GU, 2, false>(M, K, N, plan, a16, rowscale, w0, cs0, inv0, w1, cs1, inv1, out, partials, st);
+      e = nv_launch<FMT, GU, 2, false, ABF>(M, K, N, plan, a16, rowscale, w0, cs0, inv0, w1, cs1, inv1, out, partials, st);
       break;
     default:
-      e = nv_launch<FMT, GU, 4, false>(M, K, N, plan, a16, rowscale, w0, cs0, inv0, w1, cs1, inv1, out, partials, st);
+      e = nv_launch<FMT, GU, 4, false, ABF>(M, K, N, plan, a16, rowscale, w0, cs0, inv0, w1, cs1, inv1, out, partials, st);
       break;
   }
   if (e != hipSuccess || plan.units == 0) return e;
@@ -946,23 +960,34 @@ size_t mfma_partial_bytes(int fmt, int M, int K, int N, bool gu) {
   return nv_partial_bytes(nv_plan(fmt, M, K, N, gu), gu);
 }
 
+bool mfma_bf16_ok(int fmt, int K) { return fmt == 0 && K >= g_min_k(0); }
+
 hipError_t launch_mfma_gateup(int fmt, int M, int K, int N, const uint16_t* x16, const float* rowscale,
                               const uint8_t* w0, const float* cs0, float inv0, const uint8_t* w1,
-                              const float* cs1, float inv1, uint16_t* act16, float* partials, hipStream_t st) {
+                              const float* cs1, float inv1, uint16_t* act16, float* partials, bool abf,
+                              hipStream_t st) {
+  if (abf) {
+    if (!mfma_bf16_ok(fmt, K) || rowscale != nullptr) return hipErrorInvalidValue;
+    return nv_dispatch<0, true, true>(M, K, N, x16, nullptr, w0, cs0, inv0, w1, cs1, inv1, act16, partials, st);
+  }
   if (K >= g_min_k(fmt))
-    return fmt == 1 ? nv_dispatch<1, true>(M, K, N, x16, rowscale, w0, cs0, inv0, w1, cs1, inv1, act16, partials, st)
-                    : nv_dispatch<0, true>(M, K, N, x16, rowscale, w0, cs0, inv0, w1, cs1, inv1, act16, partials, st);
+    return fmt == 1 ? nv_dispatch<1, true, false>(M, K, N, x16, rowscale, w0, cs0, inv0, w1, cs1, inv1, act16, partials, st)
+                    : nv_dispatch<0, true, false>(M, K, N, x16, rowscale, w0, cs0, inv0, w1, cs1, inv1, act16, partials, st);
   if (fmt == 1)
     return gemm_dispatch<1, true>(M, K, N, x16, rowscale, w0, cs0, inv0, w1, cs1, inv1, act16, st);
   return gemm_dispatch<0, true>(M, K, N, x16, rowscale, w0, cs0, inv0, w1, cs1, inv1, act16, st);
 }
 
 hipError_t launch_mfma_linear(int fmt, int M, int K, int N, const uint16_t* a16, const float* rowscale,
-                              const uint8_t* w, const float* cs, float inv, float* y, float* partials,
+                              const uint8_t* w, const float* cs, float inv, float* y, float* partials, bool abf,
                               hipStream_t st) {
+  if (abf) {
+    if (!mfma_bf16_ok(fmt, K) || rowscale != nullptr) return hipErrorInvalidValue;
+    return nv_dispatch<0, false, true>(M, K, N, a16, nullptr, w, cs, inv, nullptr, nullptr, 0.f, y, partials, st);
+  }
   if (K >= g_min_k(fmt))
-    return fmt == 1 ? nv_dispatch<1, false>(M, K, N, a16, rowscale, w, cs, inv, nullptr, nullptr, 0.f, y, partials, st)
-                    : nv_dispatch<0, false>(M, K, N, a16, rowscale, w, cs, inv, nullptr, nullptr, 0.f, y, partials, st);
+    return fmt == 1 ? nv_dispatch<1, false, false>(M, K, N, a16, rowscale, w, cs, inv, nullptr, nullptr, 0.f, y, partials, st)
+                    : nv_dispatch<0, false, false>(M, K, N, a16, rowscale, w, cs, inv, nullptr, nullptr, 0.f, y, partials, st);
   if (fmt == 1) return gemm_dispatch<1, false>(M, K, N, a16, rowscale, w, cs, inv, nullptr, nullptr, 0.f, y, st);
   return gemm_dispatch<0, false>(M, K, N, a16, rowscale, w, cs, inv, nullptr, nullptr, 0.f, y, st);
 }
