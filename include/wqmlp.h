@@ -24,7 +24,8 @@
  *     then the device/pointer/arch checks).  A failed launch returns
  *     WQ_ELAUNCH and wq_last_hip_error() gives the hipError_t.  There is no
  *     fallback path of any kind.
- *   - M == 0 (no activation rows) is a valid empty call: WQ_OK, nothing enqueued.
+ *   - M == 0 (no activation rows) is a valid empty call: WQ_OK, nothing enqueued; the weights are
+ *     still checked, while x, the output and the workspace may be NULL.
  */
 #ifndef WQMLP_H
 #define WQMLP_H

@@ -119,6 +119,11 @@ def test_fp8_validation(L, kw, rc):
 
 def test_empty_batch_is_ok(L):
     assert L.mlp_fp8w_run(*fp8_args(M=0)) == 0
+    # an empty batch may pass NULL activations, output and workspace; the weights are still checked
+    assert L.mlp_fp8w_run(*fp8_args(M=0, x=None, out=None, ws=None, wsb=0)) == 0
+    assert L.mlp_fp8w_run(*fp8_args(M=0, wg=None)) == EINVAL
+    assert L.qlinear_run(1, 0, 64, 64, None, 1, A + 4096, None, 1.0, None, 0, None, 0, None) == 0
+    assert L.qlinear_run(1, 0, 64, 64, None, 1, None, None, 1.0, None, 0, None, 0, None) == EINVAL
 
 
 def nv_args(**kw):

@@ -179,13 +179,14 @@ int mlp_run(int fmt, int64_t M, int64_t H, int64_t I, const void* x, int x_dtype
   if (H <= 0 || I <= 0 || H > kMaxDim || I > kMaxDim || !elems_ok(M, H, I)) return WQ_EINVAL;
   const int path = mlp_path(fmt, M, H, I, flags);
   if (!shape_ok(fmt, path, H, I, x_dtype)) return WQ_EINVAL;
-  if (any_null({x, wg, wu, wd, out})) return WQ_EINVAL;
+  if (any_null({wg, wu, wd})) return WQ_EINVAL;
   if (fmt == WQ_FMT_FP8W && any_null({sg, su, sd})) return WQ_EINVAL;
   if (fmt == WQ_FMT_NVFP4) {
     for (float g : {gg, gu, gd})
       if (!(g > 0.f) || !std::isfinite(g)) return WQ_EINVAL;
   }
-  if (M == 0) return WQ_OK;
+  if (M == 0) return WQ_OK;   // nothing to do: x, out and the workspace may be null
+  if (any_null({x, out})) return WQ_EINVAL;
   if (!all_aligned({x, wg, wu, wd, out, ws})) return WQ_EALIGN;
   if (fmt == WQ_FMT_FP8W && !all_aligned({sg, su, sd})) return WQ_EALIGN;
   const size_t need = mlp_ws(fmt, M, H, I, flags & 3);
@@ -397,10 +398,11 @@ int qlinear_run(int fmt, int64_t M, int64_t N, int64_t K, const void* x, int x_d
     return WQ_EINVAL;
   }
   if (path == WQ_PATH_GEMV && !gemv_fits(fmt, K, x_dtype)) return WQ_EINVAL;
-  if (any_null({x, w, y})) return WQ_EINVAL;
+  if (w == nullptr) return WQ_EINVAL;
   if (fmt == WQ_FMT_FP8W && scale == nullptr) return WQ_EINVAL;
   if (fmt == WQ_FMT_NVFP4 && (!(global_scale > 0.f) || !std::isfinite(global_scale))) return WQ_EINVAL;
-  if (M == 0) return WQ_OK;
+  if (M == 0) return WQ_OK;   // nothing to do: x, y and the workspace may be null
+  if (any_null({x, y})) return WQ_EINVAL;
   if (!all_aligned({x, w, y, scale, workspace})) return WQ_EALIGN;
   const size_t need = qlinear_workspace_bytes(fmt, M, N, K, flags);
   if (need && (workspace == nullptr || workspace_bytes < need)) return WQ_EWORKSPACE;
