@@ -59,6 +59,10 @@ def parse():
                     help="only run this many plain NVFP4 M=512 prefill steps, for rocprofv3 --pmc passes")
     ap.add_argument("--decode-counters", type=int, default=0,
                     help="only run this many plain NVFP4 M=1 decode steps (8 rotating weight copies), for rocprofv3")
+    ap.add_argument("--fp8-prefill-counters", type=int, default=0,
+                    help="only run this many plain FP8 M=512 prefill steps (bf16 x, 2 weight copies), for rocprofv3")
+    ap.add_argument("--awq-counters", type=int, default=0,
+                    help="only run this many plain routed-expert steps over rotating experts, for rocprofv3")
     ap.add_argument("--json-out", default=None)
     return ap.parse_args()
 
@@ -221,7 +225,9 @@ def nvfp4_run(torch, wq, synth, blk, gs, M, K, copies, outlier):
     return dict(t=t, K=K, M=M, gu_ms=gu_ms, dn_ms=dn_ms, copies=copies)
 
 
-def awq_run(torch, wq, synth, K):
+def awq_run(torch, wq, synth, K, calls=0):
+    """Routed-expert step, hot and rotating experts, timed as graphs of K steps; with calls > 0 only that
+    many plain rotating-expert steps are run (for rocprofv3)."""
     dev = torch.device("cuda:0")
     d = synth.awq_moe()
     E, topk, HH, II = 512, 10, 2560, 160
@@ -237,6 +243,11 @@ def awq_run(torch, wq, synth, K):
     rot = [torch.from_numpy(r).to(dev) for r in synth.awq_rotating_ids(48, topk, E)]
     act = torch.empty((topk, II), dtype=torch.float16, device=dev)
     out = torch.empty((HH,), dtype=torch.float16, device=dev)
+    if calls:
+        for i in range(calls):
+            wq.moe_awq_m1_run(x, rot[i % len(rot)], rw, b13, b2, E, II, 3, act=act, out=out)
+        torch.cuda.synchronize()
+        return dict(calls=calls)
     res = {}
     for mode in ("hot", "rotating"):
         def step(i, mode=mode):
@@ -376,6 +387,28 @@ def main():
             wq.mlp_nvfp4_run(x, b["gate"], gs["gate"], b["up"], gs["up"], b["down"], gs["down"], out=out, workspace=ws)
         torch.cuda.synchronize()
         log(f"nvfp4 decode counter steps done: {args.decode_counters}")
+        return
+
+    if args.fp8_prefill_counters:
+        import numpy as np
+        d = synth.fp8_mlp(M=1)
+        names = ("w_gate", "s_gate", "w_up", "s_up", "w_down", "s_down")
+        base = [torch.from_numpy(d[n]).to(dev) for n in names]
+        sets = [base, [t.clone() for t in base]]
+        M = 512
+        xb = synth.to_bf16_bits(synth.rng(2, synth.T_X, (M,)).standard_normal((M, H), dtype=np.float32))
+        x = torch.from_numpy(xb.view("int16")).to(dev).view(torch.bfloat16)
+        out = torch.empty((M, H), dtype=torch.float32, device=dev)
+        ws = torch.empty(wq.mlp_workspace_bytes(wq.WQ_FMT_FP8W, M, H, I), dtype=torch.uint8, device=dev)
+        for i in range(args.fp8_prefill_counters):
+            wq.mlp_fp8w_run(x, *sets[i % 2], out=out, workspace=ws)
+        torch.cuda.synchronize()
+        log(f"fp8 prefill counter steps done: {args.fp8_prefill_counters}")
+        return
+
+    if args.awq_counters:
+        a = awq_run(torch, wq, synth, 48, calls=args.awq_counters)
+        log(f"routed-expert counter steps done: {a['calls']}")
         return
 
     K, W = args.steps, args.warmup
