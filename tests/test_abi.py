@@ -184,3 +184,26 @@ def test_qlinear_shape_rules(L):
         assert L.qlinear_run(fmt, 129, 67, 320, A, 1, A + 0x200000, scale, 1.0, None, 0, A + 0x400000, 0,
                              None) == EWORKSPACE
         assert wq.qlinear_workspace_bytes(fmt, 129, 67, 320) > 0
+
+
+def test_header_and_library_from_c(tmp_path):
+    # the boundary needs no Python: the header compiles as C99 and a C program links the library and calls it
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    libdir = os.path.join(root, "weight_quantized_mlp_amd")
+    src = tmp_path / "use.c"
+    src.write_text('#include "wqmlp.h"\n#include <stdio.h>\n'
+                   "int main(void) {\n"
+                   "  size_t ws = mlp_workspace_bytes(WQ_FMT_NVFP4, 1, 5120, 17408, WQ_PATH_AUTO);\n"
+                   '  printf("%d %zu %s\\n", wq_abi_version(), ws, wq_strerror(WQ_EINVAL));\n'
+                   "  return ws == 17408 * 2 ? 0 : 1;\n}\n")
+    exe = tmp_path / "use"
+    subprocess.run([cc, "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-I", os.path.join(root, "include"),
+                    str(src), "-o", str(exe), "-L", libdir, "-lwqmlp", "-Wl,-rpath," + libdir], check=True)
+    p = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert p.returncode == 0, p.stdout + p.stderr
+    assert p.stdout.split()[0] == str(wq.lib().wq_abi_version())
