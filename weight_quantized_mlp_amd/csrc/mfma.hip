@@ -525,12 +525,18 @@ __global__ void __launch_bounds__(256, 2) nv_gemm_kernel(int M, int K, int N, Nv
     }
     woff[j] = (uint32_t)(min(n0 + 32 * wave + c, N - 1) - nw0) * rb + 16u * (uint32_t)q;
   }
+  // Copy i of a wave moves tile rows 8 wave + 32 i .. + 7.  Under the block schedule (which waits for all
+  // of a wave's copies at once) copies whose rows all lie past M are skipped: those rows' outputs are
+  // never stored, so their LDS rows may hold anything.  The stepped schedule counts copies in its waits
+  // and always issues them.
   auto copy_a = [&](int kt, int stage) {
     kt = min(kt, nk - 1);
     const uint8_t* base = a_tile + (size_t)kt * 128;
     const uint32_t sb = lds0 + stage * kNvAStage;
 #pragma unroll
-    for (int i = 0; i < MB; ++i) lds_copy16(aoff[i], base, __builtin_amdgcn_readfirstlane(sb + (256 * i + 64 * wave) * 16));
+    for (int i = 0; i < MB; ++i)
+      if (!BS || m0 + 8 * wave + 32 * i < M)
+        lds_copy16(aoff[i], base, __builtin_amdgcn_readfirstlane(sb + (256 * i + 64 * wave) * 16));
   };
   // A row whose K-step count r = nk % KSB is not 0 ends in a short block: it is copied as the last CB
   // bytes of the row (steps KSB - r .. KSB - 1 of the window are the valid ones; K >= g_min_k, so the
