@@ -225,7 +225,7 @@ def nvfp4_run(torch, wq, synth, blk, gs, M, K, copies, outlier):
     return dict(t=t, K=K, M=M, gu_ms=gu_ms, dn_ms=dn_ms, copies=copies)
 
 
-def awq_run(torch, wq, synth, K, calls=0):
+def awq_run(torch, wq, synth, K, calls=0, layout=3):
     """Routed-expert step, hot and rotating experts, timed as graphs of K steps; with calls > 0 only that
     many plain rotating-expert steps are run (for rocprofv3)."""
     dev = torch.device("cuda:0")
@@ -233,7 +233,7 @@ def awq_run(torch, wq, synth, K, calls=0):
     E, topk, HH, II = 512, 10, 2560, 160
     def bank(codes, scales, zeros):   # the library's packer, on the device
         return wq.awq_pack_bank(torch.from_numpy(codes).to(dev), torch.from_numpy(scales.view("int16")).to(dev),
-                                torch.from_numpy(zeros).to(dev), 3)
+                                torch.from_numpy(zeros).to(dev), layout)
     b13 = bank(*d["w13"])
     b2 = bank(*d["w2"])
     torch.cuda.synchronize()
@@ -245,20 +245,20 @@ def awq_run(torch, wq, synth, K, calls=0):
     out = torch.empty((HH,), dtype=torch.float16, device=dev)
     if calls:
         for i in range(calls):
-            wq.moe_awq_m1_run(x, rot[i % len(rot)], rw, b13, b2, E, II, 3, act=act, out=out)
+            wq.moe_awq_m1_run(x, rot[i % len(rot)], rw, b13, b2, E, II, layout, act=act, out=out)
         torch.cuda.synchronize()
         return dict(calls=calls)
     res = {}
     for mode in ("hot", "rotating"):
         def step(i, mode=mode):
             ids = hot if mode == "hot" else rot[i % len(rot)]
-            wq.moe_awq_m1_run(x, ids, rw, b13, b2, E, II, 3, act=act, out=out)
+            wq.moe_awq_m1_run(x, ids, rw, b13, b2, E, II, layout, act=act, out=out)
         step(0)
         torch.cuda.synchronize()
         g = GraphBench(torch, step, K)
         g.replay_timed()
         res[mode] = g.replay_timed() / K
-    step_bytes = topk * (2 * II * HH // 2 + 3 * 2 * II * HH // 32 + HH * II // 2 + 3 * HH * II // 32)
+    step_bytes = topk * (2 * II * HH // 2 + layout * 2 * II * HH // 32 + HH * II // 2 + layout * HH * II // 32)
     return dict(hot_s=res["hot"], rot_s=res["rotating"], step_bytes=step_bytes, K=K)
 
 
@@ -426,7 +426,7 @@ def main():
     extras = {}
     want = set() if args.extras == "none" else (
         {"nvfp4_decode", "nvfp4_prefill_512", "nvfp4_prefill_8192", "nvfp4_batch8", "fp8_batch8", "fp8_prefill_512",
-         "awq"} if args.extras == "all"
+         "awq", "awq4"} if args.extras == "all"
         else set(args.extras.split(",")))
     if want & {"fp8_batch8", "fp8_prefill_512"}:
         fp8_bytes = 3 * H * I + 4 * (2 * I + H)
@@ -479,6 +479,14 @@ def main():
             extras[f"torch_f16_matmul_{M}"] = dict(ms_per_step=round(ms, 4), TFLOPs=round(tfl, 1),
                                                    mfma_frac_f16_peak=round(tfl / MFMA_F16_PEAK_TFLOPS, 4))
             log(f"torch f16 matmul M={M}", extras[f"torch_f16_matmul_{M}"])
+    if "awq4" in want:
+        a = awq_run(torch, wq, synth, 480, layout=4)
+        extras["awq_moe_m1_layout4"] = dict(
+            hot_us_per_step=round(a["hot_s"] * 1e6, 3), rotating_us_per_step=round(a["rot_s"] * 1e6, 3),
+            rotating_GBps=round(a["step_bytes"] / a["rot_s"] / 1e9, 1),
+            hot_ms_per_48=round(a["hot_s"] * 48e3, 4), rotating_ms_per_48=round(a["rot_s"] * 48e3, 4),
+            step_bytes=a["step_bytes"])
+        log("awq layout 4", extras["awq_moe_m1_layout4"])
     if "awq" in want:
         a = awq_run(torch, wq, synth, 480)
         extras["awq_moe_m1"] = dict(
