@@ -117,6 +117,13 @@ def test_fp8_validation(L, kw, rc):
     assert L.mlp_fp8w_run(*fp8_args(**kw)) == rc
 
 
+def test_flag_combinations(L):
+    # path bits 3 (both paths) and both stage bits together are invalid, as are unknown bits
+    assert L.mlp_fp8w_run(*fp8_args(flags=3)) == EINVAL
+    assert L.mlp_fp8w_run(*fp8_args(flags=4 | 8)) == EINVAL
+    assert L.mlp_fp8w_run(*fp8_args(flags=16)) == EINVAL
+
+
 def test_empty_batch_is_ok(L):
     assert L.mlp_fp8w_run(*fp8_args(M=0)) == 0
     # an empty batch may pass NULL activations, output and workspace; the weights are still checked

@@ -7,6 +7,7 @@
 * A NaN weight code (E4M3 0x7F, as a FP8 code or as an NVFP4 group scale) turns its dot products into
   NaN: in gate it reaches every output (the down projection sums all of act), in down only its own output
   column.  The NaN positions must be the oracle's.
+* The two-stage form (WQ_STAGE_GATEUP_ONLY, then WQ_STAGE_DOWN_ONLY on the same workspace) equals one call.
 """
 import numpy as np
 import pytest
@@ -113,3 +114,33 @@ def test_nan_codes_match_the_oracle(path, where):
     ref = oracle.mlp_nvfp4_ref(x64, blk["gate"], gs["gate"], blk["up"], gs["up"], blk["down"], gs["down"])
     y = run_nv(blk, gs, bf16_dev(xb), path)
     assert np.array_equal(np.isnan(y), np.isnan(ref)) and np.isnan(ref).any(), "nvfp4"
+
+
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("M", [1, 130])
+def test_split_stages_equal_one_call(path, M):
+    # WQ_STAGE_GATEUP_ONLY leaves act in the workspace; WQ_STAGE_DOWN_ONLY on the same workspace finishes
+    # the MLP: the two calls give the bits of one full call
+    xb = synth.to_bf16_bits(np.random.default_rng(35 + M).standard_normal((M, H)).astype(np.float32))
+    x = bf16_dev(xb)
+    d = fp8_weights()
+    W = [dev(d[n]) for n in FP8_NAMES]
+    blk, gs = nvfp4_weights()
+    B = {n: dev(b) for n, b in blk.items()}
+    for fmt in ("fp8", "nvfp4"):
+        f = wq.WQ_FMT_FP8W if fmt == "fp8" else wq.WQ_FMT_NVFP4
+        ws = torch.empty(max(wq.mlp_workspace_bytes(f, M, H, I, path), 1), dtype=torch.uint8, device=DEV)
+        full = torch.empty((M, H), dtype=torch.float32, device=DEV)
+        split = torch.full((M, H), float("nan"), dtype=torch.float32, device=DEV)
+
+        def run(out, stage):
+            if fmt == "fp8":
+                wq.mlp_fp8w_run(x, *W, out=out, workspace=ws, path=path, stage=stage)
+            else:
+                wq.mlp_nvfp4_run(x, B["gate"], gs["gate"], B["up"], gs["up"], B["down"], gs["down"], out=out,
+                                 workspace=ws, path=path, stage=stage)
+        run(full, None)
+        run(split, "gateup")
+        assert torch.isnan(split).all(), fmt        # the gate/up stage leaves the output alone
+        run(split, "down")
+        assert np.array_equal(host(full).view(np.uint32), host(split).view(np.uint32)), fmt
