@@ -68,7 +68,7 @@ enum { WQ_PATH_AUTO = 0, WQ_PATH_GEMV = 1, WQ_PATH_MFMA = 2 };
  * that interleave work or timing between the two stages. */
 enum { WQ_STAGE_GATEUP_ONLY = 4, WQ_STAGE_DOWN_ONLY = 8 };
 #define WQ_MFMA_MIN_ROWS 128
-#define WQ_NARROW_MIN_ROWS_NVFP4 4
+#define WQ_NARROW_MIN_ROWS_NVFP4 3
 #define WQ_NARROW_MIN_ROWS_FP8 2
 #define WQ_NARROW_MIN_WEIGHT_BYTES (16u << 20)
 /* largest top-k the routed-expert step accepts */

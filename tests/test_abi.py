@@ -60,14 +60,14 @@ def test_workspace_queries(L):
         assert base < wq.mlp_workspace_bytes(fmt, 4, 5120, 17408, "mfma") <= base + (64 << 20)
     # AUTO on short batches: the MFMA GEMM from the format's row threshold, for large weights only
     gemv = lambda fmt, M, I: M * I * (2 if fmt == 1 else 4)    # act: float16 (NVFP4) / float32 (FP8)
-    assert wq.mlp_workspace_bytes(1, 3, 5120, 17408) == gemv(1, 3, 17408)
-    assert wq.mlp_workspace_bytes(1, 4, 5120, 17408) == wq.mlp_workspace_bytes(1, 4, 5120, 17408, "mfma")
+    assert wq.mlp_workspace_bytes(1, 2, 5120, 17408) == gemv(1, 2, 17408)
+    assert wq.mlp_workspace_bytes(1, 3, 5120, 17408) == wq.mlp_workspace_bytes(1, 3, 5120, 17408, "mfma")
     assert wq.mlp_workspace_bytes(0, 1, 5120, 17408) == gemv(0, 1, 17408)
     assert wq.mlp_workspace_bytes(0, 2, 5120, 17408) == wq.mlp_workspace_bytes(0, 2, 5120, 17408, "mfma")
     assert wq.mlp_workspace_bytes(1, 64, 256, 512) == gemv(1, 64, 512)           # 0.2 MB of weights
     assert wq.mlp_workspace_bytes(0, 64, 5120 + 16, 17408) == gemv(0, 64, 17408)   # H not a multiple of 64
-    assert wq.qlinear_workspace_bytes(1, 3, 5120, 17408) == 0
-    assert wq.qlinear_workspace_bytes(1, 4, 5120, 17408) > 0
+    assert wq.qlinear_workspace_bytes(1, 2, 5120, 17408) == 0
+    assert wq.qlinear_workspace_bytes(1, 3, 5120, 17408) > 0
     assert wq.mlp_workspace_bytes(7, 1, 64, 64) == 0
     assert wq.mlp_workspace_bytes(0, 0, 64, 64) == 0
     assert wq.qlinear_workspace_bytes(1, 4, 64, 64) == 0

@@ -195,7 +195,7 @@ def test_nvfp4_paths_agree_with_oracle(nv_big, M):
         ys[path] = host(nv_run(dblk, gs, bf16_dev(xb), path=path))
         gate(ys[path], ref, what=f"nvfp4 M={M} {path}")
     # AUTO takes the GEMV below WQ_NARROW_MIN_ROWS_NVFP4 rows and the MFMA GEMM from there on
-    want = "gemv" if M < 4 else "mfma"
+    want = "gemv" if M < 3 else "mfma"
     assert np.array_equal(host(nv_run(dblk, gs, bf16_dev(xb))).view(np.uint32), ys[want].view(np.uint32))
 
 
