@@ -184,8 +184,9 @@ def test_nvfp4_prefill_M8192_sampled(nv_big):
 
 
 # M spans the short-batch tiles of the MFMA path: 32-row tiles with the block schedule (M <= 32 for
-# gate/up, M <= 128 for down, 1..4 row tiles), 64- and 128-row stepped tiles, split-K at every size.
-@pytest.mark.parametrize("M", [2, 3, 8, 17, 32, 37, 64, 96, 127, 128, 200])
+# gate/up, M <= 96 for down, 1..3 row tiles), 64-row stepped tiles (gate/up 33..64, down 97..128) and
+# 128-row ones, split-K at every size.
+@pytest.mark.parametrize("M", [2, 3, 8, 17, 32, 37, 64, 96, 97, 112, 127, 128, 200])
 def test_nvfp4_paths_agree_with_oracle(nv_big, M):
     blk, gs, W, dblk = nv_big
     xb, _ = synth.nvfp4_x(M, outlier_frac=0.05)
