@@ -835,10 +835,17 @@ __global__ void __launch_bounds__(256, 2) nv_gemm_kernel(int M, int K, int N, Nv
 
 // Epilogue of the split tiles: element (row, col) of split tile i adds its S parts in part order.
 // A thread handles 4 consecutive columns of one tile row (16-byte partial loads); workgroup b handles 1024
-// elements of split tile b / (bm / 8) (a tile has bm * 128 elements).  Stores are vectors when N is a
+// elements of split tile b / per_tile (a tile has bm * 128 elements).  Stores are vectors when N is a
 // multiple of 4 and all 4 columns exist, else per column.
 // Column factors as in the GEMM: cs0[n] / cs1[n] (FP8) when cs0 is not null, else inv0 / inv1.
 constexpr int kFinishCols = 4;
+// Workgroups per split tile: enough for the tile's rows below M when the whole batch lies in one tile
+// row (short batches), else the whole tile.  bm * 128 is a multiple of 1024, so the covered elements stay
+// inside the partial tile.
+__host__ __device__ inline int nv_finish_per_tile(int M, const NvPlan& plan) {
+  const int rows = (plan.ntm == 1 && M < plan.bm) ? M : plan.bm;
+  return (rows * 128 + 256 * kFinishCols - 1) / (256 * kFinishCols);
+}
 template <bool GU>
 __global__ void __launch_bounds__(256) nv_splitk_finish(int M, int N, NvPlan plan, const float* __restrict__ partials,
                                                        const float* __restrict__ rowscale,
@@ -846,7 +853,7 @@ __global__ void __launch_bounds__(256) nv_splitk_finish(int M, int N, NvPlan pla
                                                        const float* __restrict__ cs1, float inv1,
                                                        void* __restrict__ out) {
   constexpr int NM = GU ? 2 : 1;
-  const int per_tile = plan.bm * 128 / (256 * kFinishCols);   // workgroups per split tile
+  const int per_tile = nv_finish_per_tile(M, plan);          // workgroups per split tile
   const int i = (int)blockIdx.x / per_tile;                   // split tile index
   const int e = (((int)blockIdx.x - i * per_tile) * 256 + (int)threadIdx.x) * kFinishCols;
   const int pt = plan.bm * 128;
@@ -931,7 +938,7 @@ hipError_t nv_dispatch(int M, int K, int N, const uint16_t* a16, const float* ro
       break;
   }
   if (e != hipSuccess || plan.units == 0) return e;
-  hipLaunchKernelGGL((nv_splitk_finish<GU>), dim3((plan.tiles - plan.full) * (plan.bm * 128 / (256 * kFinishCols))),
+  hipLaunchKernelGGL((nv_splitk_finish<GU>), dim3((plan.tiles - plan.full) * nv_finish_per_tile(M, plan)),
                      dim3(256), 0, st, M, N,
                      plan, partials, rowscale, cs0, inv0, cs1, inv1, out);
   return hipGetLastError();
