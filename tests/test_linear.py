@@ -66,3 +66,27 @@ def test_auto_tail_case_is_the_gemm():
     a = host(wq.qlinear_run(wq.WQ_FMT_NVFP4, x, blk, None, float(gs), path="auto"))
     b = host(wq.qlinear_run(wq.WQ_FMT_NVFP4, x, blk, None, float(gs), path="mfma"))
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+@pytest.mark.parametrize("rows", [5, 37])
+@pytest.mark.parametrize("fmt", ["fp8", "nvfp4"])
+def test_short_batch_ragged_n_split_k(fmt, rows):
+    # A batch inside one tile row (32- or 64-row tile) with N = 67: one column tile, so the K range is
+    # split and the finish launches workgroups for the batch's rows only and stores column by column.
+    N, K = 67, 320
+    x = x_rows(17 + rows, K)[:rows]
+    if fmt == "fp8":
+        r = np.random.default_rng(19)
+        w = r.standard_normal((N, K)).astype(np.float32) * 0.05
+        s = (np.abs(w).max(axis=1) / 448).astype(np.float32)
+        codes = synth.to_e4m3_codes(w / s[:, None])
+        ref = x.astype(np.float64) @ oracle.fp8w_dequant(codes, s).T
+        y = host(wq.qlinear_run(wq.WQ_FMT_FP8W, dev(x).to(torch.bfloat16), dev(codes), dev(s), path="mfma"))
+    else:
+        wp, ws, gs = synth.nvfp4_tensor(N, K, 21, 1)
+        blk = oracle.block64_pack(wp, ws)
+        ref = x.astype(np.float64) @ oracle.nvfp4_dequant(blk, gs).T
+        y = host(wq.qlinear_run(wq.WQ_FMT_NVFP4, dev(x).to(torch.bfloat16), dev(blk), None, float(gs), path="mfma"))
+    assert y.shape == (rows, N)
+    gate(y, ref, what=f"{fmt} linear {rows}x{N}x{K} mfma")
+    assert np.all(np.isfinite(y))
