@@ -214,3 +214,57 @@ def test_header_and_library_from_c(tmp_path):
     p = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
     assert p.returncode == 0, p.stdout + p.stderr
     assert p.stdout.split()[0] == str(wq.lib().wq_abi_version())
+
+
+def _plan_partial_bytes(fmt, M, K, N, gu, slots=512, cap=64 << 20):
+    # The split-K plan restated from its definition (host logic): (32*MB)x128 tiles, MB from the batch;
+    # an underfilled last round (or fewer tiles than slots) is split along K into S parts of whole weight
+    # blocks (4 records NVFP4, 2 K steps FP8): the most parts that fit one round when two or more do,
+    # else S minimising ceil(tail*S/slots)/S; parts never empty; partial scratch capped at 64 MiB.
+    mb = (1 if M <= 96 else 2) if (not gu and M <= 128) else (1 if M <= 32 else 2 if M <= 64 else 4)
+    bm = 32 * mb
+    tiles = -(-M // bm) * -(-N // 128)
+    nblk = -(-(K // 64) // (4 if fmt == 1 else 2))
+    if tiles < slots:
+        tail = tiles
+    else:
+        tail = tiles - (-(-tiles // slots) - 1) * slots
+        if tail * 10 >= slots * 9:
+            tail = 0
+    smax = 16 if (not gu and mb == 1) else 8
+    per_part = (2 if gu else 1) * bm * 128 * 4
+    S = 1
+    if tail:
+        one = min(smax, nblk, slots // tail)
+        if one >= 2:
+            S = one
+            while S > 1 and tail * S * per_part > cap:
+                S -= 1
+        else:
+            best = 1.0
+            for s in range(2, min(smax, nblk) + 1):
+                if tail * s * per_part > cap:
+                    break
+                t = (-(-(tail * s) // slots)) / s
+                if t < best - 1e-9:
+                    best, S = t, s
+    if S < 2:
+        return 0
+    bps = -(-nblk // S)
+    return tail * -(-nblk // bps) * per_part
+
+
+def test_split_plan_sizes_at_the_full_shape(L):
+    # The MFMA workspace at hidden 5120 / intermediate 17408 equals x16 + row scales + act16 + the larger
+    # partial scratch of the two GEMMs, for batches on every tile height and both sides of each switch.
+    H, I = 5120, 17408
+    a = lambda n: -(-n // 256) * 256
+    for fmt in (0, 1):
+        for M in (2, 3, 8, 32, 33, 64, 65, 96, 97, 128, 129, 512):
+            part = max(_plan_partial_bytes(fmt, M, H, I, True), _plan_partial_bytes(fmt, M, I, H, False))
+            want = a(M * H * 2) + a(M * 4) + a(M * I * 2) + a(part)
+            assert wq.mlp_workspace_bytes(fmt, M, H, I, "mfma") == want, (fmt, M)
+    # spot values of the rule: M = 8, 3 parts of 136 gate+up tiles; M = 128, 64-row down tiles in 6 parts
+    assert _plan_partial_bytes(1, 8, H, I, True) == 408 * 2 * 32 * 128 * 4
+    assert _plan_partial_bytes(1, 8, I, H, False) == 480 * 32 * 128 * 4
+    assert _plan_partial_bytes(1, 128, I, H, False) == 480 * 64 * 128 * 4
