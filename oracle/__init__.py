@@ -25,10 +25,11 @@ Pins (what ties each function to something other than itself) are in
 through the definitions (the same functions are pinned at small sizes).
 """
 from .codecs import e4m3_to_f64, e2m1_to_f64, bf16_bits_to_f64, f16_bits_to_f64
-from .dequant import fp8w_dequant, nvfp4_dequant, nvfp4_dequant_parts, awq_dequant, awq_dequant_parts
+from .dequant import (fp8w_dequant, nvfp4_dequant, nvfp4_dequant_parts, awq_dequant, awq_dequant_parts,
+                      awq_dequant_bias, awq_bias_bits)
 from .pack import (block64_pack, block64_unpack, awq_bank_layout, awq_pack_bank,
                    awq_unpack_bank)
-from .mlp import silu, swiglu_mlp, mlp_fp8w_ref, mlp_nvfp4_ref, qlinear_ref, mlp_bruteforce
+from .mlp import silu, swiglu_mlp, mlp_fp8w_ref, mlp_nvfp4_ref, mlp_bruteforce
 from .moe import moe_awq_m1_ref, moe_w13_stage_ref, moe_w2_stage_ref, moe_bruteforce
 from .metric import normwise_rel_err
 

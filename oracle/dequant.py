@@ -53,28 +53,48 @@ def nvfp4_dequant(blk, global_scale):
     return nvfp4_dequant_parts(wp, ws, global_scale)
 
 
-def awq_dequant_parts(codes, scales_bits, zeros):
-    """AWQ int4 group-32 -> float16 bits.
+def awq_dequant_bias(codes, scales_bits, bias_bits):
+    """AWQ int4 group-32 from a stored per-group bias -> float16 bits.
 
-    dq = RN_f16(q * s + RN_f16(-z * s)): one fused multiply-add in half
-    precision with the bias -z*s rounded to half first (page "[Kernel][SM70]
-    Add native-g32 AWQ QPN M1 operator", section "What it does": the
-    half_fma(q, scale, half(-zero*scale)) boundary, not half((q-zero)*scale)).
-    codes: uint8 [..., N, K] in 0..15; scales_bits: uint16 (f16 bits) [..., N, K/32];
-    zeros: uint8 [..., N, K/32].  Returns uint16 f16 bits [..., N, K].
-    The float64 expression is exact (spans < 53 bits), so casting to float16
-    applies the single rounding of the fused operation.
+    dq = RN_f16(q * s + b) with b the float16 group bias: one fused multiply-add
+    in half precision (page "[Kernel][SM70] Add native-g32 AWQ QPN M1 operator",
+    section "What it does": the half_fma(q, scale, half(-zero*scale)) boundary;
+    the 4-byte {scale, bias} metadata stores that half bias directly).
+    codes: uint8 [..., N, K] in 0..15; scales_bits, bias_bits: uint16 (f16 bits)
+    [..., N, K/32].  Returns uint16 f16 bits [..., N, K].  q * s + b is exact in
+    float64 (q < 16 and two half operands span far fewer than 53 bits), so the
+    cast to float16 is the single rounding of the fused operation.
     """
     q = np.asarray(codes).astype(np.float64)
-    s = f16_bits_to_f64(scales_bits)
-    z = np.asarray(zeros).astype(np.float64)
-    bias = f16_bits_to_f64(f64_to_f16_bits(-z * s))
-    sk = np.repeat(s, 32, axis=-1)
-    bk = np.repeat(bias, 32, axis=-1)
+    sk = np.repeat(f16_bits_to_f64(scales_bits), 32, axis=-1)
+    bk = np.repeat(f16_bits_to_f64(bias_bits), 32, axis=-1)
     return f64_to_f16_bits(q * sk + bk)
 
 
+def awq_bias_bits(scales_bits, zeros):
+    """The group bias RN_f16(-z * s) as float16 bits (the exact float64 product, rounded once)."""
+    s = f16_bits_to_f64(scales_bits)
+    z = np.asarray(zeros).astype(np.float64)
+    return f64_to_f16_bits(-z * s)
+
+
+def awq_dequant_parts(codes, scales_bits, zeros):
+    """AWQ int4 group-32 from (codes, scales, uint8 zeros) -> float16 bits.
+
+    dq = RN_f16(q * s + RN_f16(-z * s)) (same section as above: the bias is the
+    zero times the scale, negated and rounded to half, then one half fma; not
+    half((q-zero)*scale)).  zeros: uint8 [..., N, K/32].
+    """
+    return awq_dequant_bias(codes, scales_bits, awq_bias_bits(scales_bits, zeros))
+
+
 def awq_dequant(bank, E, N, K, meta_layout=3):
-    """Prepared bank -> f16 bits [E, N, K] (unpacks the documented bank layout)."""
-    codes, scales, zeros = awq_unpack_bank(bank, E, N, K, meta_layout)
-    return awq_dequant_parts(codes, scales, zeros)
+    """Prepared bank -> f16 bits [E, N, K] (unpacks the documented bank layout).
+
+    meta_layout 3 stores uint8 zeros and the bias is formed from them;
+    meta_layout 4 stores the float16 bias itself, which is used as read.
+    """
+    codes, scales, meta = awq_unpack_bank(bank, E, N, K, meta_layout)
+    if meta_layout == 3:
+        return awq_dequant_parts(codes, scales, meta)
+    return awq_dequant_bias(codes, scales, meta)

@@ -74,11 +74,6 @@ def mlp_nvfp4_ref(x, gblk, ggs, ublk, ugs, dblk, dgs, return_act=False, rows_blo
     return (out, act) if return_act else out
 
 
-def qlinear_ref(x, W):
-    """y = x W^T in float64 (one quantised linear with dequantised W)."""
-    return np.asarray(x, dtype=np.float64) @ np.asarray(W, dtype=np.float64).T
-
-
 def mlp_bruteforce(x, Wg, Wu, Wd):
     """Pure-Python triple loop of the same definition, for tiny shapes only.
 

@@ -98,7 +98,7 @@ def awq_unpack_bank(bank, E, N, K, meta_layout=3):
     """Inverse of awq_pack_bank -> (codes [E,N,K], scales f16 bits [E,N,G], zeros u8 [E,N,G]).
 
     For meta_layout 4 the zero is not stored; the third value returned is
-    then the f16 bias bits, and awq_dequant_parts is not applicable as is.
+    then the f16 bias bits [E,N,G] (decode them with dequant.awq_dequant_bias).
     """
     L = awq_bank_layout(N, K, meta_layout)
     G = L["G"]

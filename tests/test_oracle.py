@@ -226,6 +226,32 @@ def test_awq_one_hot_boundary_reads(kk):
     assert set(nz[:, 2]) == {kk} and np.all(dq[:, :, kk] == 0.75)
 
 
+def test_awq_layout4_bank_decodes_like_the_parts():
+    # the 4-byte layout stores RN_f16(-z*s) itself; decoding it must give the 3-byte layout's values bitwise
+    d = synth.awq_moe(E=3, topk=2, H=128, I=64)
+    for name, (E, N, K) in (("w13", (3, 128, 128)), ("w2", (3, 128, 64))):
+        c, s, z = d[name]
+        want = dequant.awq_dequant_parts(c, s, z)
+        for layout in (3, 4):
+            got = dequant.awq_dequant(pack.awq_pack_bank(c, s, z, layout), E, N, K, layout)
+            assert np.array_equal(got, want), (name, layout)
+
+
+@pytest.mark.parametrize("kk", [int(v) for v in golden("awq_one_hot_k.txt")["indices"].split()])
+def test_awq_layout4_one_hot_boundary_reads(kk):
+    # the same K indices as the 3-byte case, read through the stored-bias layout; a distinct non-zero
+    # bias (z = 3) on every group makes a misplaced bias plane visible
+    E, N, K = 2, 8, int(golden("awq_one_hot_k.txt")["K"])
+    codes = np.full((E, N, K), 3, dtype=np.uint8)
+    zeros = np.full((E, N, K // 32), 3, dtype=np.uint8)                 # q == z -> exactly 0
+    scales = np.full((E, N, K // 32), np.float16(0.125)).view(np.uint16)
+    scales[:, :, kk // 32] = np.float16(0.5).view(np.uint16)            # the hot group's own scale
+    codes[:, :, kk] = 9
+    dq = codecs.f16_bits_to_f64(dequant.awq_dequant(pack.awq_pack_bank(codes, scales, zeros, 4), E, N, K, 4))
+    nz = np.argwhere(dq != 0)
+    assert set(nz[:, 2]) == {kk} and np.all(dq[:, :, kk] == 3.0)        # (9 - 3) * 0.5
+
+
 # ---- MLP ------------------------------------------------------------------------------------------
 def test_silu_closed_forms():
     z = np.array([-800.0, -30.0, -1.0, 0.0, 1.0, 30.0, 800.0])
@@ -327,6 +353,76 @@ def test_moe_special_cases():
     _, y = moe.moe_w2_stage_ref(act, d["ids"], d["router_w"], *d["w2"])
     assert np.array_equal(y[0], y[1])
     assert np.array_equal(out, (codecs.f16_bits_to_f64(y[0]) * 0.75).astype(np.float16).view(np.uint16))
+
+
+# ---- the parity metric ---------------------------------------------------------------------------------
+# Hand-computed cases of the row-normwise error  max_m ( max_o |y - r| / max_o |r| ), with the row scale
+# min_m max_o |r| returned beside it.  Each tuple: (y, ref, expected error, expected min row scale).
+METRIC_CASES = [
+    ([[1.0, 2.0]], [[1.0, 2.5]], 0.5 / 2.5, 2.5),                         # one row
+    ([[1000.0, 0.0], [1.01, -1.0]], [[1000.0, 0.0], [1.0, -1.0]], 0.01, 1.0),   # each row on its own scale
+    ([[4.0, 2e-6]], [[4.0, 1e-6]], 1e-6 / 4.0, 4.0),                       # a tiny element is not its own scale
+    ([[-3.3, 1.0]], [[-3.0, 1.0]], 0.3 / 3.0, 3.0),                        # magnitudes, not signed values
+    ([[1.0, 1.0], [1.0, 1.0], [1.3, 1.0]], [[1.0, 1.0]] * 3, 0.3, 1.0),    # the worst row, not the mean
+    ([[2.0]], [[1.0]], 1.0, 1.0),                                          # the reference is the denominator
+    ([[0.0, 0.0], [2.0, 0.0]], [[0.0, 0.0], [2.0, 0.5]], 0.25, 0.0),       # exact zero row: error 0, scale 0
+    ([1.0, 3.0], [1.0, 4.0], 0.25, 4.0),                                   # 1-D input is one row
+]
+
+
+def _metric_failures(fn):
+    """The METRIC_CASES (and the non-finite ones) that fn gets wrong."""
+    bad = []
+    for i, (y, r, want, want_scale) in enumerate(METRIC_CASES):
+        err, scale = fn(np.array(y), np.array(r))
+        if not (abs(err - want) <= 1e-12 * max(1.0, want) and abs(scale - want_scale) <= 1e-12):
+            bad.append(i)
+    err, _ = fn(np.array([[0.0, 1e-30]]), np.array([[0.0, 0.0]]))          # any error on a zero row fails
+    if not np.isinf(err):
+        bad.append("zero-row")
+    return bad
+
+
+def test_normwise_metric_hand_computed():
+    assert _metric_failures(oracle.normwise_rel_err) == []
+
+
+def test_normwise_metric_pins_catch_planted_metrics():
+    def as_rows(y, r):
+        return np.atleast_2d(np.asarray(y, float)), np.atleast_2d(np.asarray(r, float))
+
+    def global_norm(y, r):          # one scale for the whole matrix: under-reports small rows
+        y, r = as_rows(y, r)
+        with np.errstate(divide="ignore", invalid="ignore"):
+            return float(np.max(np.abs(y - r)) / np.max(np.abs(r))), float(np.min(np.max(np.abs(r), axis=1)))
+
+    def mean_rows(y, r):            # mean over rows instead of the worst row
+        y, r = as_rows(y, r)
+        s = np.max(np.abs(r), axis=1)
+        with np.errstate(divide="ignore", invalid="ignore"):
+            return float(np.mean(np.max(np.abs(y - r), axis=1) / s)), float(np.min(s))
+
+    def y_denominator(y, r):        # scaled by the result under test
+        return oracle.normwise_rel_err(r, y)
+
+    def no_abs(y, r):               # signed difference
+        y, r = as_rows(y, r)
+        s = np.max(np.abs(r), axis=1)
+        with np.errstate(divide="ignore", invalid="ignore"):
+            return float(np.max(np.max(y - r, axis=1) / s)), float(np.min(s))
+
+    def elementwise(y, r):          # per-element relative error
+        y, r = as_rows(y, r)
+        with np.errstate(divide="ignore", invalid="ignore"):
+            e = np.where(r != 0, np.abs(y - r) / np.abs(r), np.where(y != r, np.inf, 0.0))
+        return float(np.max(e)), float(np.min(np.max(np.abs(r), axis=1)))
+
+    def zero_rows_pass(y, r):       # a zero reference row forgives any error
+        err, s = oracle.normwise_rel_err(y, r)
+        return (0.0 if np.isinf(err) else err), s
+
+    for planted in (global_norm, mean_rows, y_denominator, no_abs, elementwise, zero_rows_pass):
+        assert _metric_failures(planted), planted.__name__
 
 
 # ---- planted mistakes: each must be caught by one of the pins above ---------------------------------
