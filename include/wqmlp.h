@@ -95,9 +95,11 @@ int wq_last_hip_error(void);
  *   GEMV path: act [M, I], float32 (FP8) or float16 (NVFP4).
  *   MFMA path: x as float16 [M, H] (row-scaled; unused for FP8 with bf16 x),
  *              per-row scales float32 [M],
- *              act float16 [M, I], then float32 split-K partial tiles of
- *              at most 64 MiB; each region 256-byte aligned.
- *              The size is a function of the shape alone.
+ *              act float16 [M, I] (the down GEMM's operand),
+ *              FP8 only: act float32 [M, I] and its per-row scales float32 [M],
+ *              then float32 split-K partial tiles of at most 64 MiB; each
+ *              region 256-byte aligned.  The size is a function of the shape
+ *              alone.
  */
 size_t mlp_workspace_bytes(int fmt, int64_t M, int64_t H, int64_t I, int flags);
 
@@ -121,8 +123,12 @@ size_t mlp_workspace_bytes(int fmt, int64_t M, int64_t H, int64_t I, int flags);
  * MFMA path numerics: with bf16 x the gate/up GEMM runs bf16 MFMAs on x as
  * given; float32 x is scaled per row by a power of two and rounded to float16
  * (bf16-representable values give the same bits either way); E4M3 codes decode
- * exactly; act = silu(g) * u is rounded to float16 for the down GEMM, so |act|
- * must stay below 65504.
+ * exactly; act = silu(g) * u is kept in float32 between the projections (as on
+ * the GEMV path) and the down GEMM takes it as float16 after an exact
+ * power-of-two scale per row (max |act| of the row in [2^14, 2^15)), which it
+ * takes back out of the result: any finite act is accepted; each element is
+ * rounded once (relative error at most 2^-11, or an absolute error below 2^-39
+ * of the row's largest |act| for elements in float16's subnormal range).
  */
 int mlp_fp8w_run(int64_t M, int64_t H, int64_t I, const void* x, int x_dtype,
                  const uint8_t* w_gate, const float* s_gate,
@@ -163,6 +169,10 @@ int mlp_nvfp4_run(int64_t M, int64_t H, int64_t I, const void* x, int x_dtype,
 
 /*
  * Bytes of a prepared AWQ bank holding E experts of one [N, K] matrix.
+ * The metadata sizes are the pull request's ("[Kernel][SM70] Add native-g32
+ * AWQ QPN M1 operator", section "What it does": a 3-byte {FP16 scale, u8 zero}
+ * and a 4-byte {FP16 scale, FP16 bias} layout per group of 32); the pull
+ * request gives no byte order, so the order below is this library's own.
  * Layout (per expert, experts stacked with this per-expert stride / E; every
  * plane 16-byte aligned):
  *   codes  [N][K/2] uint8: byte j of row n holds k=2j (low nibble), 2j+1 (high)
@@ -220,18 +230,31 @@ int nvfp4_pack_block64(int64_t N, int64_t K, const uint8_t* weight_packed,
  *   codes  [E, N, K] uint8 in 0..15 (one code per byte)
  *   scales [E, N, K/32] float16 bits
  *   zeros  [E, N, K/32] uint8
- * bank must hold awq_bank_bytes(E, N, K, meta_layout) bytes.
+ * meta_layout 3 stores the zeros; meta_layout 4 stores bias = RN_f16(-zero * scale),
+ * the half bias of the dequantisation boundary (pull request "[Kernel][SM70] Add
+ * native-g32 AWQ QPN M1 operator", section "What it does"), so both layouts decode
+ * to the same values.  bank must hold awq_bank_bytes(E, N, K, meta_layout) bytes
+ * and be 16-byte aligned; the inputs need no alignment.  One-time, device to device.
  */
 int awq_pack_bank(int64_t E, int64_t N, int64_t K, const uint8_t* codes,
                   const uint16_t* scales, const uint8_t* zeros, int meta_layout,
                   void* bank, void* stream);
 
-/* Debug decoders: the same __device__ decode as the kernels, written out.      */
-/* out[n,k] = RN_f32(e4m3(w[n,k]) * s[n])                              [N, K] f32 */
+/*
+ * Debug decoders: each weight decoded on its own, one element per thread.  They use
+ * the float32 conversions of the float32-activation GEMV kernels and the AWQ
+ * kernels' half fma; the kernels that take bfloat16 or float16 operands decode with
+ * the packed bfloat16 / float16 conversions instead, which these calls do not run
+ * (the one-hot read-outs through qlinear_run and the MLP's gate/up stage reach those).
+ */
+/* FP8 ("tp>1 fp8w tail-MLP shard ...", section "Mechanism on the tp>1 path"):
+ * out[n,k] = RN_f32(e4m3(w[n,k]) * s[n])                              [N, K] f32 */
 int fp8w_dequant_f32(int64_t N, int64_t K, const uint8_t* w, const float* s, float* out, void* stream);
-/* out[n,k] = RN_f32(e2m1(q) * e4m3(d) * RN_f32(1/global_scale))        [N, K] f32 */
+/* NVFP4 (page "Qwen3.8-27B-NVFP4", section "NVFP4 numerics as implemented"):
+ * out[n,k] = RN_f32(e2m1(q) * e4m3(d) * RN_f32(1/global_scale))        [N, K] f32 */
 int nvfp4_dequant_f32(int64_t N, int64_t K, const uint8_t* blk, float global_scale, float* out, void* stream);
-/* out[e,n,k] = dq as in moe_awq_m1_run                            [E, N, K] f16 bits */
+/* AWQ (pull request "[Kernel][SM70] Add native-g32 AWQ QPN M1 operator", section
+ * "What it does"): out[e,n,k] = dq as in moe_awq_m1_run          [E, N, K] f16 bits */
 int awq_dequant_f16(int64_t E, int64_t N, int64_t K, const void* bank, int meta_layout,
                     uint16_t* out, void* stream);
 
@@ -240,7 +263,12 @@ int awq_dequant_f16(int64_t E, int64_t N, int64_t K, const void* bank, int meta_
  * kernels as the MLP's down projection (GEMV) or its MFMA GEMM.
  *   fmt WQ_FMT_FP8W: w = [N, K] E4M3 codes, scale = [N] float32, global_scale ignored
  *   fmt WQ_FMT_NVFP4: w = Block64 [N, K/64], scale = NULL, global_scale as above
- *   y [M, N] float32.  Workspace: qlinear_workspace_bytes.
+ *   x [M, K]: WQ_F32 or WQ_BF16; WQ_F16 for NVFP4 on the GEMV path only (the
+ *   operand type of the NVFP4 MLP's down projection; AUTO then always takes the
+ *   GEMV, and WQ_PATH_MFMA with it is WQ_EINVAL).
+ *   y [M, N] float32.  Workspace: qlinear_workspace_bytes (the GEMV path needs
+ *   none; the query does not know x's type and may ask for more than a float16
+ *   call uses).
  * Shapes: K a positive multiple of 64 for NVFP4 and for the MFMA path, else of
  * 16; N any positive row count (partial tiles are masked, as in the tail case of
  * page "Qwen3.8-27B-NVFP4", section "Correctness and precision": 129 x 67 x 320).

@@ -107,12 +107,14 @@ def _need(t, name, dtype, dev=None, numel=None):
     return t
 
 
-def _xdtype(x):
+def _xdtype(x, allow_f16=False):
     if x.dtype == torch.float32:
         return WQ_F32
     if x.dtype == torch.bfloat16:
         return WQ_BF16
-    raise TypeError("x must be float32 or bfloat16")
+    if allow_f16 and x.dtype == torch.float16:
+        return WQ_F16
+    raise TypeError("x must be float32 or bfloat16" + (" (or float16 for NVFP4)" if allow_f16 else ""))
 
 
 def wq_abi_version():
@@ -134,9 +136,20 @@ def _workspace(nbytes, dev, workspace):
     return workspace
 
 
+def _stage_flags(stage, workspace):
+    """Stage bits; a one-stage call must bring the workspace that carries act between the two stages."""
+    if stage not in _STAGES:
+        raise ValueError(f"stage must be one of {list(_STAGES)}")
+    if stage is not None and workspace is None:
+        raise ValueError("stage='gateup' or 'down' needs the caller's workspace: act is handed from the "
+                         "gate/up stage to the down stage through it")
+    return _STAGES[stage]
+
+
 def mlp_fp8w_run(x, w_gate, s_gate, w_up, s_up, w_down, s_down, out=None, workspace=None, path="auto",
                  stage=None):
     """FP8 E4M3 per-channel SwiGLU MLP.  x [M,H] f32/bf16; w_gate/w_up [I,H] u8; w_down [H,I] u8; s_* f32."""
+    sflags = _stage_flags(stage, workspace)
     dev = x.device
     M, H = x.shape
     I = w_gate.shape[0]
@@ -152,7 +165,7 @@ def mlp_fp8w_run(x, w_gate, s_gate, w_up, s_up, w_down, s_down, out=None, worksp
     ws = _workspace(nb, dev, workspace)
     rc = lib().mlp_fp8w_run(M, H, I, _ptr(x), _xdtype(x), _ptr(w_gate), _ptr(s_gate), _ptr(w_up), _ptr(s_up),
                             _ptr(w_down), _ptr(s_down), _ptr(ws), ws.numel(), _ptr(out),
-                            _PATHS[path] | _STAGES[stage], _stream(dev))
+                            _PATHS[path] | sflags, _stream(dev))
     _check("mlp_fp8w_run", rc)
     return out
 
@@ -160,6 +173,7 @@ def mlp_fp8w_run(x, w_gate, s_gate, w_up, s_up, w_down, s_down, out=None, worksp
 def mlp_nvfp4_run(x, gate_blk, gate_gs, up_blk, up_gs, down_blk, down_gs, out=None, workspace=None, path="auto",
                   stage=None):
     """NVFP4 Block64 SwiGLU MLP.  x [M,H]; gate/up_blk [I,H/64,36] u8; down_blk [H,I/64,36] u8; gs floats."""
+    sflags = _stage_flags(stage, workspace)
     dev = x.device
     M, H = x.shape
     I = gate_blk.shape[0]
@@ -174,7 +188,7 @@ def mlp_nvfp4_run(x, gate_blk, gate_gs, up_blk, up_gs, down_blk, down_gs, out=No
     ws = _workspace(nb, dev, workspace)
     rc = lib().mlp_nvfp4_run(M, H, I, _ptr(x), _xdtype(x), _ptr(gate_blk), float(gate_gs), _ptr(up_blk),
                              float(up_gs), _ptr(down_blk), float(down_gs), _ptr(ws), ws.numel(), _ptr(out),
-                             _PATHS[path] | _STAGES[stage], _stream(dev))
+                             _PATHS[path] | sflags, _stream(dev))
     _check("mlp_nvfp4_run", rc)
     return out
 
@@ -284,9 +298,9 @@ def qlinear_run(fmt, x, w, scale=None, global_scale=1.0, N=None, path="auto", ou
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=dev)
     _need(out, "out", torch.float32, dev, M * N)
-    nb = qlinear_workspace_bytes(fmt, M, N, K, path)
+    nb = 0 if x.dtype == torch.float16 else qlinear_workspace_bytes(fmt, M, N, K, path)
     ws = _workspace(nb, dev, workspace) if nb else None
-    rc = lib().qlinear_run(fmt, M, N, K, _ptr(x), _xdtype(x), _ptr(w), _ptr(scale), float(global_scale), _ptr(ws),
+    rc = lib().qlinear_run(fmt, M, N, K, _ptr(x), _xdtype(x, allow_f16=True), _ptr(w), _ptr(scale), float(global_scale), _ptr(ws),
                            0 if ws is None else ws.numel(), _ptr(out), _PATHS[path], _stream(dev))
     _check("qlinear_run", rc)
     return out

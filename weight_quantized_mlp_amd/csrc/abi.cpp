@@ -147,12 +147,39 @@ size_t mlp_partials(int fmt, int64_t M, int64_t H, int64_t I) {
 // float16 for NVFP4.
 size_t act_gemv_bytes(int fmt) { return fmt == WQ_FMT_NVFP4 ? 2 : 4; }
 
+// Byte offsets of the MFMA path's workspace regions (each 256-byte aligned, in this order):
+//   x16 [M,H] float16 (row-scaled x), rs [M] float32 (x row scales), act16 [M,I] float16 (the down
+//   GEMM's operand); FP8 only: act32 [M,I] float32 (act as the gate/up stage produced it) and ars [M]
+//   float32 (act row scales); then the split-K partial tiles.
+struct MfmaWs {
+  size_t x16, rs, act16, act32, ars, partials, total;
+};
+MfmaWs mfma_ws(int fmt, int64_t M, int64_t H, int64_t I) {
+  MfmaWs w{};
+  size_t o = 0;
+  w.x16 = o;
+  o += align256((size_t)M * H * 2);
+  w.rs = o;
+  o += align256((size_t)M * 4);
+  w.act16 = o;
+  o += align256((size_t)M * I * 2);
+  if (fmt == WQ_FMT_FP8W) {
+    w.act32 = o;
+    o += align256((size_t)M * I * 4);
+    w.ars = o;
+    o += align256((size_t)M * 4);
+  }
+  w.partials = o;
+  o += align256(mlp_partials(fmt, M, H, I));
+  w.total = o;
+  return w;
+}
+
 // Workspace of the two-layer MLP; 0 means "invalid".
 size_t mlp_ws(int fmt, int64_t M, int64_t H, int64_t I, int flags) {
   if (M <= 0 || H <= 0 || I <= 0 || M > kMaxDim || H > kMaxDim || I > kMaxDim || !elems_ok(M, H, I)) return 0;
   if (mlp_path(fmt, M, H, I, flags) == WQ_PATH_GEMV) return align256((size_t)M * I * act_gemv_bytes(fmt));
-  return align256((size_t)M * H * 2) + align256((size_t)M * 4) + align256((size_t)M * I * 2) +
-         align256(mlp_partials(fmt, M, H, I));
+  return mfma_ws(fmt, M, H, I).total;
 }
 
 bool shape_ok(int fmt, int path, int64_t H, int64_t I, int x_dtype) {
@@ -217,29 +244,36 @@ int mlp_run(int fmt, int64_t M, int64_t H, int64_t I, const void* x, int x_dtype
     return rc;
   }
   uint8_t* base = reinterpret_cast<uint8_t*>(ws);
-  uint16_t* x16 = reinterpret_cast<uint16_t*>(base);
-  float* rs = reinterpret_cast<float*>(base + align256((size_t)M * H * 2));
-  uint16_t* act16 = reinterpret_cast<uint16_t*>(base + align256((size_t)M * H * 2) + align256((size_t)M * 4));
-  float* partials = mlp_partials(fmt, M, H, I)
-                        ? reinterpret_cast<float*>(base + align256((size_t)M * H * 2) + align256((size_t)M * 4) +
-                                                   align256((size_t)M * I * 2))
-                        : nullptr;
+  const MfmaWs L = mfma_ws(fmt, M, H, I);
+  uint16_t* x16 = reinterpret_cast<uint16_t*>(base + L.x16);
+  float* rs = reinterpret_cast<float*>(base + L.rs);
+  uint16_t* act16 = reinterpret_cast<uint16_t*>(base + L.act16);
+  // FP8: the gate/up stage stores act as float32 (no rounding between the projections, as the FP8
+  // definition asks); the down stage makes its float16 operand with an exact power-of-two row scale and
+  // takes the scale back out in its epilogue, so no act value can overflow.  NVFP4: act16 directly.
+  float* act32 = fmt == WQ_FMT_FP8W ? reinterpret_cast<float*>(base + L.act32) : nullptr;
+  float* ars = fmt == WQ_FMT_FP8W ? reinterpret_cast<float*>(base + L.ars) : nullptr;
+  void* act_out = fmt == WQ_FMT_FP8W ? static_cast<void*>(act32) : static_cast<void*>(act16);
+  float* partials = mlp_partials(fmt, M, H, I) ? reinterpret_cast<float*>(base + L.partials) : nullptr;
   const int f = fmt == WQ_FMT_NVFP4 ? 1 : 0;
   if (do_gu) {
     // FP8 with bf16 x: bf16 MFMAs on x as given; otherwise x is row-scaled to float16 first
     if (xt == wq::X_BF16 && wq::mfma_bf16_ok(f, h)) {
       rc = launched(wq::launch_mfma_gateup(f, m, h, i, reinterpret_cast<const uint16_t*>(x), nullptr, wg, sg, 0.f,
-                                           wu, su, 0.f, act16, partials, true, st));
+                                           wu, su, 0.f, act_out, partials, true, st));
     } else {
       rc = launched(wq::launch_rowscale_f16(m, h, x, xt, x16, rs, st));
       if (rc == WQ_OK)
         rc = launched(wq::launch_mfma_gateup(f, m, h, i, x16, rs, wg, sg, f ? 1.0f / gg : 0.f, wu, su,
-                                             f ? 1.0f / gu : 0.f, act16, partials, false, st));
+                                             f ? 1.0f / gu : 0.f, act_out, partials, false, st));
     }
   }
-  if (rc == WQ_OK && do_down)
-    rc = launched(wq::launch_mfma_linear(f, m, i, h, act16, nullptr, wd, sd, f ? 1.0f / gd : 0.f, out, partials,
-                                         false, st));
+  if (rc == WQ_OK && do_down) {
+    if (fmt == WQ_FMT_FP8W) rc = launched(wq::launch_rowscale_f16(m, i, act32, wq::X_F32, act16, ars, st));
+    if (rc == WQ_OK)
+      rc = launched(wq::launch_mfma_linear(f, m, i, h, act16, ars, wd, sd, f ? 1.0f / gd : 0.f, out, partials,
+                                           false, st));
+  }
   return rc;
 }
 
@@ -387,9 +421,11 @@ int qlinear_run(int fmt, int64_t M, int64_t N, int64_t K, const void* x, int x_d
                 void* stream) {
   if (fmt != WQ_FMT_FP8W && fmt != WQ_FMT_NVFP4) return WQ_EINVAL;
   if (flags < WQ_PATH_AUTO || flags > WQ_PATH_MFMA) return WQ_EINVAL;
-  if (x_dtype != WQ_F32 && x_dtype != WQ_BF16) return WQ_EINVAL;
+  if (x_dtype != WQ_F32 && x_dtype != WQ_BF16 && x_dtype != WQ_F16) return WQ_EINVAL;
+  // float16 x: the operand type of the NVFP4 MLP's GEMV down projection; NVFP4 on the GEMV path only
+  if (x_dtype == WQ_F16 && (fmt != WQ_FMT_NVFP4 || flags == WQ_PATH_MFMA)) return WQ_EINVAL;
   if (M < 0 || M > kMaxDim || N <= 0 || K <= 0 || N > kMaxDim || K > kMaxDim || !elems_ok(M, N, K)) return WQ_EINVAL;
-  const int path = linear_path(fmt, M, N, K, flags);
+  const int path = x_dtype == WQ_F16 ? WQ_PATH_GEMV : linear_path(fmt, M, N, K, flags);
   // K runs along the records (NVFP4), the 64-wide MFMA K steps and the 16-byte FP8 chunks; N (output
   // rows) is free: every kernel clamps its row loads to N-1 and guards its stores
   if (path == WQ_PATH_MFMA || fmt == WQ_FMT_NVFP4) {
@@ -404,7 +440,7 @@ int qlinear_run(int fmt, int64_t M, int64_t N, int64_t K, const void* x, int x_d
   if (M == 0) return WQ_OK;   // nothing to do: x, y and the workspace may be null
   if (any_null({x, y})) return WQ_EINVAL;
   if (!all_aligned({x, w, y, scale, workspace})) return WQ_EALIGN;
-  const size_t need = qlinear_workspace_bytes(fmt, M, N, K, flags);
+  const size_t need = path == WQ_PATH_GEMV ? 0 : qlinear_workspace_bytes(fmt, M, N, K, flags);
   if (need && (workspace == nullptr || workspace_bytes < need)) return WQ_EWORKSPACE;
   const size_t ns = fmt == WQ_FMT_FP8W ? (size_t)N * 4 : 0;
   if (any_overlap({{y, (size_t)M * N * 4}, {workspace, need}},
@@ -413,7 +449,7 @@ int qlinear_run(int fmt, int64_t M, int64_t N, int64_t K, const void* x, int x_d
   int rc = check_device({x, w, scale, need ? workspace : nullptr, y});
   if (rc != WQ_OK) return rc;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const wq::XType xt = x_dtype == WQ_BF16 ? wq::X_BF16 : wq::X_F32;
+  const wq::XType xt = x_dtype == WQ_BF16 ? wq::X_BF16 : (x_dtype == WQ_F16 ? wq::X_F16 : wq::X_F32);
   const float inv = fmt == WQ_FMT_NVFP4 ? 1.0f / global_scale : 0.f;
   if (path == WQ_PATH_GEMV) {
     if (fmt == WQ_FMT_FP8W)

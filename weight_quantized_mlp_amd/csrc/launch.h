@@ -56,11 +56,13 @@ hipError_t launch_fast_nvfp4(int M, int K, int N, const void* x, XType xt, const
                              const uint8_t* b1, float inv1, void* y, bool y16, hipStream_t st);
 
 // ---- M >= 128: MFMA GEMM family ---------------------------------------------------------------
-// x [M,K] (f32 or bf16) -> x16 [M,K] f16 scaled per row by 2^-e, rowscale[m] = 2^e.
+// x [M,K] (f32 or bf16) -> x16 [M,K] f16 scaled per row by 2^-e, rowscale[m] = 2^e, where max_k |x[m,k]| * 2^-e
+// lies in [2^14, 2^15); every K that is a multiple of 64.
 hipError_t launch_rowscale_f16(int M, int K, const void* x, XType xt, uint16_t* x16, float* rowscale,
                                hipStream_t st);
 // fmt 0 FP8 (w = [N,K] codes, colscale[n]) / 1 NVFP4 (w = Block64, uniform inv).
-// gate+up: act16[m,n] = f16(silu(g) * u) with g = rowscale[m]*colscale(n)*acc.
+// gate+up: act[m,n] = silu(g) * u with g = rowscale[m]*colscale(n)*acc, stored as float32 (FP8) or rounded to
+// float16 (NVFP4).
 // partials: float32 scratch of mfma_partial_bytes(fmt, M, K, N, gu) bytes (NULL allowed when that is 0);
 // the NVFP4 GEMM splits the tiles of an underfilled last round along K and finishes them from there.
 // abf: the activations are bfloat16 bits as given (rowscale must be null) and the GEMM runs bf16 MFMAs;
@@ -70,7 +72,7 @@ bool mfma_bf16_ok(int fmt, int K);
 hipError_t launch_mfma_gateup(int fmt, int M, int K, int N, const uint16_t* x16, const float* rowscale,
                               const uint8_t* w0, const float* cs0, float inv0,
                               const uint8_t* w1, const float* cs1, float inv1,
-                              uint16_t* act16, float* partials, bool abf, hipStream_t st);
+                              void* act, float* partials, bool abf, hipStream_t st);
 // single matrix: y[m,n] = rowscale[m] (1 if null) * colscale(n) * sum_k a16[m,k] dq(w[n,k]).
 hipError_t launch_mfma_linear(int fmt, int M, int K, int N, const uint16_t* a16, const float* rowscale,
                               const uint8_t* w, const float* cs, float inv, float* y, float* partials, bool abf,

@@ -15,8 +15,12 @@
 //     6 significant bits (the K=16 rescale is folded into every decoded weight), and
 //     every E4M3 value is a float16;
 //   * gate/up: acc * 2^e_m * (1/global_scale or channel scale), act = silu(g) * u in
-//     float32, rounded once to float16 for the down GEMM (|act| < 65504 required);
-//   * down: acc * (1/global_scale or channel scale), stored as float32.
+//     float32.  FP8: act is stored as float32 (the FP8 definition keeps act unrounded
+//     between the two projections) and the down GEMM's operand is made from it by the
+//     same exact power-of-two row scaling as x, so no act value can overflow float16.
+//     NVFP4: act is rounded once to float16 (|act| < 65504 required);
+//   * down: acc * (act row scale, FP8) * (1/global_scale or channel scale), stored as
+//     float32.
 //
 // Tiling (both kernels): a workgroup of 4 waves computes a (32*MB) x 128 output tile (of both gate and
 // up for the fused projection).  All waves share the activation tile, staged in LDS; each wave owns 32
@@ -99,6 +103,42 @@ struct RowChunk<float> {      // 4 float32
   }
 };
 
+// Power-of-two row scale e: max |x| * 2^-e lies in [2^14, 2^15) (e = 0 for a zero or non-finite max).
+__device__ __forceinline__ int row_pow2_exp(float amax) {
+  int e = 0;
+  if (amax > 0.f && amax <= 3.0e38f) {
+    int ex;
+    (void)frexpf(amax, &ex);   // amax = f * 2^ex, f in [0.5, 1)
+    e = ex - 15;                // amax * 2^-e in [2^14, 2^15)
+    e = e < -100 ? -100 : (e > 100 ? 100 : e);
+  }
+  return e;
+}
+template <typename XT>
+__device__ __forceinline__ float chunk_absmax(u32x4 v, float amax) {
+  constexpr int E = RowChunk<XT>::E;
+  float f[E];
+  RowChunk<XT>::unpack(v, f);
+#pragma unroll
+  for (int j = 0; j < E; ++j) amax = fmaxf(amax, fabsf(f[j]));
+  return amax;
+}
+// Chunk c of a row, scaled by 2^-e and rounded to float16, stored at chunk c of the float16 row o.
+template <typename XT>
+__device__ __forceinline__ void put_scaled(uint16_t* o, int c, u32x4 v, int e) {
+  constexpr int E = RowChunk<XT>::E;
+  float f[E];
+  RowChunk<XT>::unpack(v, f);
+  uint32_t hh[E / 2];
+#pragma unroll
+  for (int j = 0; j < E / 2; ++j) {
+    const _Float16 lo = (_Float16)ldexpf(f[2 * j], -e), hi = (_Float16)ldexpf(f[2 * j + 1], -e);
+    hh[j] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+  }
+  if constexpr (E == 8) reinterpret_cast<u32x4*>(o)[c] = u32x4{hh[0], hh[1], hh[2], hh[3]};
+  else reinterpret_cast<u32x2*>(o)[c] = u32x2{hh[0], hh[1]};
+}
+
 template <typename XT, int RC>
 __global__ void __launch_bounds__(256) rowscale_f16_kernel(int M, int K, const XT* __restrict__ x,
                                                            uint16_t* __restrict__ x16,
@@ -117,52 +157,64 @@ __global__ void __launch_bounds__(256) rowscale_f16_kernel(int M, int K, const X
   }
   float amax = 0.f;
 #pragma unroll
-  for (int i = 0; i < RC; ++i) {
-    float f[E];
-    RowChunk<XT>::unpack(cache[i], f);
-#pragma unroll
-    for (int j = 0; j < E; ++j) amax = fmaxf(amax, fabsf(f[j]));
-  }
-  for (int c = lane + 64 * RC; c < nch; c += 64) {
-    float f[E];
-    RowChunk<XT>::unpack(xr[c], f);
-#pragma unroll
-    for (int j = 0; j < E; ++j) amax = fmaxf(amax, fabsf(f[j]));
-  }
+  for (int i = 0; i < RC; ++i) amax = chunk_absmax<XT>(cache[i], amax);
+  for (int c = lane + 64 * RC; c < nch; c += 64) amax = chunk_absmax<XT>(xr[c], amax);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
-  int e = 0;
-  if (amax > 0.f && amax <= 3.0e38f) {
-    int ex;
-    (void)frexpf(amax, &ex);   // amax = f * 2^ex, f in [0.5, 1)
-    e = ex - 15;                // amax * 2^-e in [2^14, 2^15)
-    e = e < -100 ? -100 : (e > 100 ? 100 : e);
-  }
+  const int e = row_pow2_exp(amax);
   if (lane == 0) rowscale[m] = ldexpf(1.0f, e);
   uint16_t* o = x16 + (size_t)m * K;
-  auto put = [&](int c, u32x4 v) {
-    float f[E];
-    RowChunk<XT>::unpack(v, f);
-    uint32_t h[E / 2];
-#pragma unroll
-    for (int j = 0; j < E / 2; ++j) {
-      const _Float16 lo = (_Float16)ldexpf(f[2 * j], -e), hi = (_Float16)ldexpf(f[2 * j + 1], -e);
-      h[j] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
-    }
-    if constexpr (E == 8) reinterpret_cast<u32x4*>(o)[c] = u32x4{h[0], h[1], h[2], h[3]};
-    else reinterpret_cast<u32x2*>(o)[c] = u32x2{h[0], h[1]};
-  };
 #pragma unroll
   for (int i = 0; i < RC; ++i) {
     const int c = lane + 64 * i;
-    if (c < nch) put(c, cache[i]);
+    if (c < nch) put_scaled<XT>(o, c, cache[i], e);
   }
-  for (int c = lane + 64 * RC; c < nch; c += 64) put(c, xr[c]);
+  for (int c = lane + 64 * RC; c < nch; c += 64) put_scaled<XT>(o, c, xr[c], e);
+}
+
+// Long rows (the MLP's act, K = intermediate): one 256-thread workgroup per row, RC chunks per thread
+// kept in registers (the rest re-read), the row max reduced across each wave and then across the four
+// waves through LDS.  Same scale and rounding as rowscale_f16_kernel.
+template <typename XT, int RC>
+__global__ void __launch_bounds__(256) rowscale_f16_wg_kernel(int M, int K, const XT* __restrict__ x,
+                                                              uint16_t* __restrict__ x16,
+                                                              float* __restrict__ rowscale) {
+  constexpr int E = RowChunk<XT>::E;
+  __shared__ float wmax[4];
+  const int m = (int)blockIdx.x;
+  const int t = (int)threadIdx.x;
+  const int nch = K / E;
+  const u32x4* xr = reinterpret_cast<const u32x4*>(x + (size_t)m * K);
+  u32x4 cache[RC];
+#pragma unroll
+  for (int i = 0; i < RC; ++i) {
+    const int c = t + 256 * i;
+    cache[i] = c < nch ? xr[c] : u32x4{0u, 0u, 0u, 0u};
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < RC; ++i) amax = chunk_absmax<XT>(cache[i], amax);
+  for (int c = t + 256 * RC; c < nch; c += 256) amax = chunk_absmax<XT>(xr[c], amax);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+  if ((t & 63) == 0) wmax[t >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  const int e = row_pow2_exp(amax);
+  if (t == 0) rowscale[m] = ldexpf(1.0f, e);
+  uint16_t* o = x16 + (size_t)m * K;
+#pragma unroll
+  for (int i = 0; i < RC; ++i) {
+    const int c = t + 256 * i;
+    if (c < nch) put_scaled<XT>(o, c, cache[i], e);
+  }
+  for (int c = t + 256 * RC; c < nch; c += 256) put_scaled<XT>(o, c, xr[c], e);
 }
 
 // ---- the GEMM ------------------------------------------------------------------------------------
 // FMT 0: FP8 E4M3 codes [N][K], per-column scale cs[n].  FMT 1: NVFP4 Block64 [N][K/64], factor inv.
-// GU: two weight matrices, out = f16 act [M][N]; else one matrix, out = f32 y [M][N].
+// GU: two weight matrices, out = act [M][N] (float32 for FP8, float16 for NVFP4); else one matrix,
+// out = f32 y [M][N].
 template <int FMT, bool GU, int MB>
 __global__ void __launch_bounds__(256, 2) mfma_gemm_kernel(int M, int K, int N, int ntm, int ntn,
                                                           const uint16_t* __restrict__ a16,
@@ -334,8 +386,9 @@ __global__ void __launch_bounds__(256, 2) mfma_gemm_kernel(int M, int K, int N, 
         if constexpr (GU) {
           const float g = acc[0][mb][r] * rs * cf[0];
           const float u = acc[1][mb][r] * rs * cf[1];
-          const _Float16 a = (_Float16)(silu_f32(g) * u);
-          reinterpret_cast<uint16_t*>(out)[(size_t)m * N + ncol] = __builtin_bit_cast(uint16_t, a);
+          const float a = silu_f32(g) * u;
+          if constexpr (FMT == 0) reinterpret_cast<float*>(out)[(size_t)m * N + ncol] = a;   // FP8: float32 act
+          else reinterpret_cast<uint16_t*>(out)[(size_t)m * N + ncol] = __builtin_bit_cast(uint16_t, (_Float16)a);
         } else {
           reinterpret_cast<float*>(out)[(size_t)m * N + ncol] = acc[0][mb][r] * rs * cf[0];
         }
@@ -823,8 +876,9 @@ __global__ void __launch_bounds__(256, 2) nv_gemm_kernel(int M, int K, int N, Nv
         if constexpr (GU) {
           const float g = acc[0][mb][r] * rs * c0;
           const float u = acc[1][mb][r] * rs * c1;
-          const _Float16 a = (_Float16)(silu_f32(g) * u);
-          reinterpret_cast<uint16_t*>(out)[(size_t)m * N + ncol] = __builtin_bit_cast(uint16_t, a);
+          const float a = silu_f32(g) * u;
+          if constexpr (FMT == 0) reinterpret_cast<float*>(out)[(size_t)m * N + ncol] = a;   // FP8: float32 act
+          else reinterpret_cast<uint16_t*>(out)[(size_t)m * N + ncol] = __builtin_bit_cast(uint16_t, (_Float16)a);
         } else {
           reinterpret_cast<float*>(out)[(size_t)m * N + ncol] = acc[0][mb][r] * rs * c0;
         }
@@ -846,7 +900,8 @@ __host__ __device__ inline int nv_finish_per_tile(int M, const NvPlan& plan) {
   const int rows = (plan.ntm == 1 && M < plan.bm) ? M : plan.bm;
   return (rows * 128 + 256 * kFinishCols - 1) / (256 * kFinishCols);
 }
-template <bool GU>
+// ACT32 (gate+up of FP8): act is stored as float32; otherwise as float16.
+template <bool GU, bool ACT32>
 __global__ void __launch_bounds__(256) nv_splitk_finish(int M, int N, NvPlan plan, const float* __restrict__ partials,
                                                        const float* __restrict__ rowscale,
                                                        const float* __restrict__ cs0, float inv0,
@@ -870,7 +925,24 @@ __global__ void __launch_bounds__(256) nv_splitk_finish(int M, int N, NvPlan pla
     for (int t = 0; t < NM; ++t) acc[t] += *reinterpret_cast<const f32x4*>(p + (size_t)s * NM * pt + t * pt);
   const float rs = rowscale ? rowscale[m] : 1.0f;
   const bool vec = (N & 3) == 0 && n + kFinishCols <= N;
-  if constexpr (GU) {
+  if constexpr (GU && ACT32) {
+    float a[kFinishCols];
+#pragma unroll
+    for (int j = 0; j < kFinishCols; ++j) {
+      const int nj = min(n + j, N - 1);
+      const float c0 = cs0 ? cs0[nj] : inv0;
+      const float c1 = cs0 ? cs1[nj] : inv1;
+      a[j] = silu_f32(acc[0][j] * rs * c0) * (acc[1][j] * rs * c1);
+    }
+    float* o = reinterpret_cast<float*>(out) + (size_t)m * N + n;
+    if (vec) {
+      *reinterpret_cast<f32x4*>(o) = f32x4{a[0], a[1], a[2], a[3]};
+    } else {
+#pragma unroll
+      for (int j = 0; j < kFinishCols; ++j)
+        if (n + j < N) o[j] = a[j];
+    }
+  } else if constexpr (GU) {
     uint16_t a[kFinishCols];
 #pragma unroll
     for (int j = 0; j < kFinishCols; ++j) {
@@ -938,7 +1010,7 @@ hipError_t nv_dispatch(int M, int K, int N, const uint16_t* a16, const float* ro
       break;
   }
   if (e != hipSuccess || plan.units == 0) return e;
-  hipLaunchKernelGGL((nv_splitk_finish<GU>), dim3((plan.tiles - plan.full) * nv_finish_per_tile(M, plan)),
+  hipLaunchKernelGGL((nv_splitk_finish<GU, GU && FMT == 0>), dim3((plan.tiles - plan.full) * nv_finish_per_tile(M, plan)),
                      dim3(256), 0, st, M, N,
                      plan, partials, rowscale, cs0, inv0, cs1, inv1, out);
   return hipGetLastError();
@@ -968,7 +1040,18 @@ hipError_t gemm_dispatch(int M, int K, int N, const uint16_t* a16, const float* 
 
 hipError_t launch_rowscale_f16(int M, int K, const void* x, XType xt, uint16_t* x16, float* rowscale,
                                hipStream_t st) {
-  // four rows (waves) per workgroup; 10 (bf16) / 20 (float32) register chunks per lane cover K = 5120
+  // Rows of up to 5120 elements: four rows (waves) per workgroup, 10 (bf16) / 20 (float32) register chunks
+  // per lane.  Longer rows: a workgroup per row, 10 / 20 register chunks per thread (K up to 20480 kept in
+  // registers).
+  if (K > 5120) {
+    if (xt == X_BF16)
+      hipLaunchKernelGGL((rowscale_f16_wg_kernel<uint16_t, 10>), dim3(M), dim3(256), 0, st, M, K,
+                         reinterpret_cast<const uint16_t*>(x), x16, rowscale);
+    else
+      hipLaunchKernelGGL((rowscale_f16_wg_kernel<float, 20>), dim3(M), dim3(256), 0, st, M, K,
+                         reinterpret_cast<const float*>(x), x16, rowscale);
+    return hipGetLastError();
+  }
   const dim3 grid((M + 3) / 4);
   if (xt == X_BF16)
     hipLaunchKernelGGL((rowscale_f16_kernel<uint16_t, 10>), grid, dim3(256), 0, st, M, K,
@@ -988,7 +1071,7 @@ bool mfma_bf16_ok(int fmt, int K) { return fmt == 0 && K >= g_min_k(0); }
 
 hipError_t launch_mfma_gateup(int fmt, int M, int K, int N, const uint16_t* x16, const float* rowscale,
                               const uint8_t* w0, const float* cs0, float inv0, const uint8_t* w1,
-                              const float* cs1, float inv1, uint16_t* act16, float* partials, bool abf,
+                              const float* cs1, float inv1, void* act16, float* partials, bool abf,
                               hipStream_t st) {
   if (abf) {
     if (!mfma_bf16_ok(fmt, K) || rowscale != nullptr) return hipErrorInvalidValue;

@@ -6,7 +6,9 @@
 // AWQ bank: the layout documented in wqmlp.h (codes row-major, float16 scale plane,
 // uint8 zero plane or float16 bias plane), metadata sizes from pull request
 // "[Kernel][SM70] Add native-g32 AWQ QPN M1 operator", section "What it does".
-// The decoders run the very __device__ decode routines of the GEMV / MFMA / MoE kernels.
+// The decoders decode one element per thread with the float32 conversions (the ones the float32-activation
+// GEMV kernels use) and the AWQ kernels' own half-fma pair decode.  Kernels with bfloat16 or float16
+// operands decode with the packed bfloat16 / float16 conversions, which these decoders do not run.
 #include "dev_common.h"
 #include "launch.h"
 
