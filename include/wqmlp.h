@@ -52,7 +52,8 @@ enum {
   WQ_EDEVICE = -4,    /* a pointer is not device memory of the current device */
   WQ_EARCH = -5,      /* the current device is not gfx950 */
   WQ_EWORKSPACE = -6, /* workspace missing or smaller than the query returns */
-  WQ_ELAUNCH = -7     /* kernel launch failed; see wq_last_hip_error() */
+  WQ_ELAUNCH = -7,    /* kernel launch failed; see wq_last_hip_error() */
+  WQ_ESCRATCH = -8    /* the call needs more than WQ_STATIC_SCRATCH_BYTES (mlp_fp8w_run_noalloc) */
 };
 /* path selection (flags bits 0-1).  AUTO picks the MFMA GEMM for M >= WQ_MFMA_MIN_ROWS, and for
  * 1 < M < WQ_MFMA_MIN_ROWS when M >= WQ_NARROW_MIN_ROWS_NVFP4 / WQ_NARROW_MIN_ROWS_FP8 (by format), the
@@ -136,6 +137,27 @@ int mlp_fp8w_run(int64_t M, int64_t H, int64_t I, const void* x, int x_dtype,
                  const uint8_t* w_down, const float* s_down,
                  void* workspace, size_t workspace_bytes, float* out,
                  int flags, void* stream);
+
+/*
+ * mlp_fp8w_run without a workspace argument, for callers that cannot allocate
+ * device memory (code under hipGraph capture, tight serving loops, harnesses that
+ * forbid allocation).  Same arguments, definition, kernels and results as
+ * mlp_fp8w_run with flags holding a WQ_PATH_* value only (stage bits are
+ * WQ_EINVAL: the two-stage form hands act over in the scratch).  The scratch is a
+ * static device array of WQ_STATIC_SCRATCH_BYTES inside the library, one per GPU,
+ * held from the library's first use on that GPU until the process ends; a call
+ * whose workspace (mlp_workspace_bytes) would exceed it returns WQ_ESCRATCH
+ * before anything is enqueued (at hidden 5120 / intermediate 17408: every M up to
+ * 32).  The call allocates nothing.  Every call on one GPU shares that GPU's
+ * scratch and leaves its contents there: calls that may overlap in time on one
+ * GPU (several streams or host threads) race, and must be ordered by the caller.
+ */
+#define WQ_STATIC_SCRATCH_BYTES ((size_t)32 << 20)
+int mlp_fp8w_run_noalloc(int64_t M, int64_t H, int64_t I, const void* x, int x_dtype,
+                         const uint8_t* w_gate, const float* s_gate,
+                         const uint8_t* w_up, const float* s_up,
+                         const uint8_t* w_down, const float* s_down,
+                         float* out, int flags, void* stream);
 
 /*
  * NVFP4 SwiGLU MLP on Block64 records.

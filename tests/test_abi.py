@@ -36,7 +36,8 @@ def test_every_declared_symbol_is_exported(L):
     assert set(names) == {
         "wq_abi_version", "wq_strerror", "wq_last_hip_error", "mlp_workspace_bytes", "mlp_fp8w_run",
         "mlp_nvfp4_run", "awq_bank_bytes", "moe_awq_m1_run", "nvfp4_pack_block64", "awq_pack_bank",
-        "fp8w_dequant_f32", "nvfp4_dequant_f32", "awq_dequant_f16", "qlinear_workspace_bytes", "qlinear_run"}
+        "fp8w_dequant_f32", "nvfp4_dequant_f32", "awq_dequant_f16", "qlinear_workspace_bytes", "qlinear_run",
+        "mlp_fp8w_run_noalloc"}
     for n in names:
         assert hasattr(L, n), n
         assert n in wq.__all__ or n == "wq_last_hip_error", n
@@ -44,7 +45,7 @@ def test_every_declared_symbol_is_exported(L):
 
 def test_version_and_messages(L):
     assert wq.wq_abi_version() == 1
-    for rc in range(0, -8, -1):
+    for rc in range(0, -9, -1):
         assert wq.wq_strerror(rc) != "unknown error"
     assert wq.wq_strerror(-99) == "unknown error"
 
@@ -252,3 +253,25 @@ def test_binding_stage_calls_need_a_workspace():
         with pytest.raises(ValueError, match="stage"):
             run(x, *([None] * 6), stage="both")
 
+
+def test_noalloc_validation(L):
+    # mlp_fp8w_run_noalloc: pure checks first; a call needing more than the static scratch is WQ_ESCRATCH
+    ESCRATCH = -8
+    H, I = 5120, 17408
+    args = lambda M, flags: (M, H, I, A, 1, A + 0x10000000, A + 0x20000000, A + 0x30000000, A + 0x40000000,
+                             A + 0x50000000, A + 0x60000000, A + 0x70000000, flags, None)
+    assert wq.mlp_workspace_bytes(0, 64, H, I) > wq.WQ_STATIC_SCRATCH_BYTES >= wq.mlp_workspace_bytes(0, 32, H, I)
+    assert L.mlp_fp8w_run_noalloc(*args(64, 0)) == ESCRATCH
+    assert L.mlp_fp8w_run_noalloc(*args(512, 0)) == ESCRATCH
+    assert L.mlp_fp8w_run_noalloc(*args(1, 4)) == EINVAL            # stage bits: whole calls only
+    assert L.mlp_fp8w_run_noalloc(*args(1, 16)) == EINVAL
+    assert L.mlp_fp8w_run_noalloc(*args(0, 0)) == 0                 # empty batch
+    a = list(args(1, 0))
+    a[3] = None
+    assert L.mlp_fp8w_run_noalloc(*a) == EINVAL                     # null x
+    a = list(args(1, 0))
+    a[11] = A + 4                                                   # misaligned out
+    assert L.mlp_fp8w_run_noalloc(*a) == EALIGN
+    a = list(args(1, 0))
+    a[11] = A + 0x10000000                                          # out on the gate weights
+    assert L.mlp_fp8w_run_noalloc(*a) == EOVERLAP

@@ -16,7 +16,7 @@ import torch
 __all__ = [
     "WQError", "lib", "lib_path", "WQ_F32", "WQ_BF16", "WQ_F16", "WQ_FMT_FP8W", "WQ_FMT_NVFP4",
     "WQ_PATH_AUTO", "WQ_PATH_GEMV", "WQ_PATH_MFMA", "WQ_STAGE_GATEUP_ONLY", "WQ_STAGE_DOWN_ONLY", "wq_abi_version", "wq_strerror",
-    "mlp_workspace_bytes", "mlp_fp8w_run", "mlp_nvfp4_run", "awq_bank_bytes", "moe_awq_m1_run",
+    "WQ_STATIC_SCRATCH_BYTES", "mlp_workspace_bytes", "mlp_fp8w_run", "mlp_fp8w_run_noalloc", "mlp_nvfp4_run", "awq_bank_bytes", "moe_awq_m1_run",
     "nvfp4_pack_block64", "awq_pack_bank", "fp8w_dequant_f32", "nvfp4_dequant_f32", "awq_dequant_f16",
     "qlinear_workspace_bytes", "qlinear_run",
 ]
@@ -25,6 +25,7 @@ WQ_F32, WQ_BF16, WQ_F16 = 0, 1, 2
 WQ_FMT_FP8W, WQ_FMT_NVFP4 = 0, 1
 WQ_PATH_AUTO, WQ_PATH_GEMV, WQ_PATH_MFMA = 0, 1, 2
 WQ_STAGE_GATEUP_ONLY, WQ_STAGE_DOWN_ONLY = 4, 8
+WQ_STATIC_SCRATCH_BYTES = 32 << 20
 _PATHS = {"auto": WQ_PATH_AUTO, "gemv": WQ_PATH_GEMV, "mfma": WQ_PATH_MFMA}
 _STAGES = {None: 0, "gateup": WQ_STAGE_GATEUP_ONLY, "down": WQ_STAGE_DOWN_ONLY}
 
@@ -42,6 +43,7 @@ _SIGS = {
     "wq_last_hip_error": (_INT, []),
     "mlp_workspace_bytes": (_SZ, [_INT, _I64, _I64, _I64, _INT]),
     "mlp_fp8w_run": (_INT, [_I64, _I64, _I64, _P, _INT, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _INT, _P]),
+    "mlp_fp8w_run_noalloc": (_INT, [_I64, _I64, _I64, _P, _INT, _P, _P, _P, _P, _P, _P, _P, _INT, _P]),
     "mlp_nvfp4_run": (_INT, [_I64, _I64, _I64, _P, _INT, _P, _F, _P, _F, _P, _F, _P, _SZ, _P, _INT, _P]),
     "awq_bank_bytes": (_SZ, [_I64, _I64, _I64, _INT]),
     "moe_awq_m1_run": (_INT, [_I64, _I64, _I64, _I64, _P, _P, _P, _P, _P, _INT, _P, _P, _P]),
@@ -167,6 +169,24 @@ def mlp_fp8w_run(x, w_gate, s_gate, w_up, s_up, w_down, s_down, out=None, worksp
                             _ptr(w_down), _ptr(s_down), _ptr(ws), ws.numel(), _ptr(out),
                             _PATHS[path] | sflags, _stream(dev))
     _check("mlp_fp8w_run", rc)
+    return out
+
+
+def mlp_fp8w_run_noalloc(x, w_gate, s_gate, w_up, s_up, w_down, s_down, out, path="auto"):
+    """mlp_fp8w_run on the library's static scratch: no workspace, and the caller passes out (nothing is
+    allocated, here or in the library).  Calls needing more than WQ_STATIC_SCRATCH_BYTES raise (WQ_ESCRATCH)."""
+    dev = x.device
+    M, H = x.shape
+    I = w_gate.shape[0]
+    _need(x, "x", x.dtype, dev)
+    for n, t, k in (("w_gate", w_gate, I * H), ("w_up", w_up, I * H), ("w_down", w_down, H * I)):
+        _need(t, n, torch.uint8, dev, k)
+    for n, t, k in (("s_gate", s_gate, I), ("s_up", s_up, I), ("s_down", s_down, H)):
+        _need(t, n, torch.float32, dev, k)
+    _need(out, "out", torch.float32, dev, M * H)
+    rc = lib().mlp_fp8w_run_noalloc(M, H, I, _ptr(x), _xdtype(x), _ptr(w_gate), _ptr(s_gate), _ptr(w_up),
+                                    _ptr(s_up), _ptr(w_down), _ptr(s_down), _ptr(out), _PATHS[path], _stream(dev))
+    _check("mlp_fp8w_run_noalloc", rc)
     return out
 
 

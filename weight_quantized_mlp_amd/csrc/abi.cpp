@@ -20,6 +20,13 @@
 #include "../../include/wqmlp.h"
 #include "launch.h"
 
+// Static scratch of mlp_fp8w_run_noalloc: one array per device, part of the library's code object; the
+// loader places it in each device's memory when the library is first used there, and it stays until the
+// process ends.  In host code `scratch` names a host-side stand-in, never the device array: its device
+// address is taken once per device with hipGetSymbolAddress (that device current, static_scratch below)
+// and only that address is handed to kernels.
+static __device__ __align__(256) uint8_t scratch[WQ_STATIC_SCRATCH_BYTES];
+
 namespace {
 
 thread_local int g_last_hip = 0;
@@ -194,10 +201,41 @@ bool shape_ok(int fmt, int path, int64_t H, int64_t I, int x_dtype) {
   return true;
 }
 
-// Shared body of the two MLP entry points.
+// ---- the static scratch of mlp_fp8w_run_noalloc (the array itself is declared at file scope above) ------
+std::once_flag g_scratch_once[kMaxDev];
+void* g_scratch_ptr[kMaxDev];
+int g_scratch_err[kMaxDev];
+
+// Device address of the current device's scratch (WQ_OK), or WQ_EDEVICE with the hipError_t recorded.
+int static_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDev) {
+    g_last_hip = (int)e;
+    return WQ_EDEVICE;
+  }
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    const hipError_t err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_err[dev] = (int)err;
+    g_scratch_ptr[dev] = err == hipSuccess ? p : nullptr;
+  });
+  if (g_scratch_ptr[dev] == nullptr) {
+    g_last_hip = g_scratch_err[dev] ? g_scratch_err[dev] : (int)hipErrorInvalidSymbol;
+    return WQ_EDEVICE;
+  }
+  *out = g_scratch_ptr[dev];
+  return WQ_OK;
+}
+
+// Shared body of the MLP entry points.
+// use_static: the workspace is the library's static scratch (ws and ws_bytes are ignored): a call that
+// needs more than WQ_STATIC_SCRATCH_BYTES is WQ_ESCRATCH, and the scratch's address is taken only after
+// every other check has passed (it is not an allocation the pointer query knows, so it is not checked).
 int mlp_run(int fmt, int64_t M, int64_t H, int64_t I, const void* x, int x_dtype, const uint8_t* wg,
             const float* sg, float gg, const uint8_t* wu, const float* su, float gu, const uint8_t* wd,
-            const float* sd, float gd, void* ws, size_t ws_bytes, float* out, int flags, void* stream) {
+            const float* sd, float gd, void* ws, size_t ws_bytes, float* out, int flags, void* stream,
+            bool use_static = false) {
   const int stage = flags & (WQ_STAGE_GATEUP_ONLY | WQ_STAGE_DOWN_ONLY);
   if ((flags & ~15) || (flags & 3) == 3 || stage == (WQ_STAGE_GATEUP_ONLY | WQ_STAGE_DOWN_ONLY)) return WQ_EINVAL;
   const bool do_gu = stage != WQ_STAGE_DOWN_ONLY, do_down = stage != WQ_STAGE_GATEUP_ONLY;
@@ -214,18 +252,24 @@ int mlp_run(int fmt, int64_t M, int64_t H, int64_t I, const void* x, int x_dtype
   }
   if (M == 0) return WQ_OK;   // nothing to do: x, out and the workspace may be null
   if (any_null({x, out})) return WQ_EINVAL;
+  if (use_static) ws = nullptr;
   if (!all_aligned({x, wg, wu, wd, out, ws})) return WQ_EALIGN;
   if (fmt == WQ_FMT_FP8W && !all_aligned({sg, su, sd})) return WQ_EALIGN;
   const size_t need = mlp_ws(fmt, M, H, I, flags & 3);
-  if (ws == nullptr || ws_bytes < need) return WQ_EWORKSPACE;
+  if (use_static) {
+    if (need > WQ_STATIC_SCRATCH_BYTES) return WQ_ESCRATCH;
+  } else if (ws == nullptr || ws_bytes < need) {
+    return WQ_EWORKSPACE;
+  }
   const size_t nx = (size_t)M * H * xsize(x_dtype);
   const size_t nw_gu = wbytes(fmt, I, H), nw_d = wbytes(fmt, H, I);
   const size_t ns_gu = fmt == WQ_FMT_FP8W ? (size_t)I * 4 : 0, ns_d = fmt == WQ_FMT_FP8W ? (size_t)H * 4 : 0;
-  if (any_overlap({{out, (size_t)M * H * 4}, {ws, need}},
+  if (any_overlap({{out, (size_t)M * H * 4}, {ws, use_static ? 0 : need}},
                   {{x, nx}, {wg, nw_gu}, {wu, nw_gu}, {wd, nw_d}, {sg, ns_gu}, {su, ns_gu}, {sd, ns_d}}))
     return WQ_EOVERLAP;
   int rc = check_device({x, wg, wu, wd, sg, su, sd, ws, out});
   if (rc != WQ_OK) return rc;
+  if (use_static && (rc = static_scratch(&ws)) != WQ_OK) return rc;
 
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const wq::XType xt = x_dtype == WQ_BF16 ? wq::X_BF16 : wq::X_F32;
@@ -293,6 +337,7 @@ const char* wq_strerror(int rc) {
     case WQ_EARCH: return "current device is not gfx950";
     case WQ_EWORKSPACE: return "workspace missing or too small";
     case WQ_ELAUNCH: return "kernel launch failed";
+    case WQ_ESCRATCH: return "call needs more scratch than the library's static scratch holds (WQ_STATIC_SCRATCH_BYTES)";
     default: return "unknown error";
   }
 }
@@ -310,6 +355,14 @@ int mlp_fp8w_run(int64_t M, int64_t H, int64_t I, const void* x, int x_dtype, co
                  void* stream) {
   return mlp_run(WQ_FMT_FP8W, M, H, I, x, x_dtype, w_gate, s_gate, 0.f, w_up, s_up, 0.f, w_down, s_down, 0.f,
                  workspace, workspace_bytes, out, flags, stream);
+}
+
+int mlp_fp8w_run_noalloc(int64_t M, int64_t H, int64_t I, const void* x, int x_dtype, const uint8_t* w_gate,
+                         const float* s_gate, const uint8_t* w_up, const float* s_up, const uint8_t* w_down,
+                         const float* s_down, float* out, int flags, void* stream) {
+  if (flags & ~3) return WQ_EINVAL;   // whole calls only: a stage split would hand act over in shared scratch
+  return mlp_run(WQ_FMT_FP8W, M, H, I, x, x_dtype, w_gate, s_gate, 0.f, w_up, s_up, 0.f, w_down, s_down, 0.f,
+                 nullptr, 0, out, flags, stream, true);
 }
 
 int mlp_nvfp4_run(int64_t M, int64_t H, int64_t I, const void* x, int x_dtype, const uint8_t* gate_blk,
