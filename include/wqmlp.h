@@ -300,6 +300,17 @@ int qlinear_run(int fmt, int64_t M, int64_t N, int64_t K, const void* x, int x_d
                 const uint8_t* w, const float* scale, float global_scale,
                 void* workspace, size_t workspace_bytes, float* y, int flags, void* stream);
 
+/*
+ * Measurement helper, not a step of the method: a plain streaming read of `bytes`
+ * (a positive multiple of 16) at src by `grid` workgroups (1 .. 2^20) of 256
+ * threads, coalesced 16-byte loads in a grid-stride loop.  Its rate is the
+ * achievable HBM read ceiling that the bandwidth-bound kernels are compared with,
+ * beside the device's published peak.  sink: grid 32-bit words of device memory,
+ * written only in the rare case that a lane's XOR fold of its data equals one fixed
+ * value (so nothing is stored in practice, yet the loads cannot be removed).
+ */
+int wq_read_probe(const void* src, size_t bytes, uint32_t* sink, int grid, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported(L):
         "wq_abi_version", "wq_strerror", "wq_last_hip_error", "mlp_workspace_bytes", "mlp_fp8w_run",
         "mlp_nvfp4_run", "awq_bank_bytes", "moe_awq_m1_run", "nvfp4_pack_block64", "awq_pack_bank",
         "fp8w_dequant_f32", "nvfp4_dequant_f32", "awq_dequant_f16", "qlinear_workspace_bytes", "qlinear_run",
-        "mlp_fp8w_run_noalloc"}
+        "mlp_fp8w_run_noalloc", "wq_read_probe"}
     for n in names:
         assert hasattr(L, n), n
         assert n in wq.__all__ or n == "wq_last_hip_error", n
@@ -275,3 +275,12 @@ def test_noalloc_validation(L):
     a = list(args(1, 0))
     a[11] = A + 0x10000000                                          # out on the gate weights
     assert L.mlp_fp8w_run_noalloc(*a) == EOVERLAP
+
+
+def test_read_probe_validation(L):
+    assert L.wq_read_probe(None, 1 << 20, A, 8, None) == EINVAL
+    assert L.wq_read_probe(A, 0, A + (1 << 30), 8, None) == EINVAL
+    assert L.wq_read_probe(A, 100, A + (1 << 30), 8, None) == EINVAL          # not a multiple of 16
+    assert L.wq_read_probe(A, 1 << 20, A + (1 << 30), 0, None) == EINVAL
+    assert L.wq_read_probe(A + 8, 1 << 20, A + (1 << 30), 8, None) == EALIGN
+    assert L.wq_read_probe(A, 1 << 20, A + 4096, 8, None) == EOVERLAP

@@ -18,7 +18,7 @@ __all__ = [
     "WQ_PATH_AUTO", "WQ_PATH_GEMV", "WQ_PATH_MFMA", "WQ_STAGE_GATEUP_ONLY", "WQ_STAGE_DOWN_ONLY", "wq_abi_version", "wq_strerror",
     "WQ_STATIC_SCRATCH_BYTES", "mlp_workspace_bytes", "mlp_fp8w_run", "mlp_fp8w_run_noalloc", "mlp_nvfp4_run", "awq_bank_bytes", "moe_awq_m1_run",
     "nvfp4_pack_block64", "awq_pack_bank", "fp8w_dequant_f32", "nvfp4_dequant_f32", "awq_dequant_f16",
-    "qlinear_workspace_bytes", "qlinear_run",
+    "qlinear_workspace_bytes", "qlinear_run", "wq_read_probe",
 ]
 
 WQ_F32, WQ_BF16, WQ_F16 = 0, 1, 2
@@ -54,6 +54,7 @@ _SIGS = {
     "awq_dequant_f16": (_INT, [_I64, _I64, _I64, _P, _INT, _P, _P]),
     "qlinear_workspace_bytes": (_SZ, [_INT, _I64, _I64, _I64, _INT]),
     "qlinear_run": (_INT, [_INT, _I64, _I64, _I64, _P, _INT, _P, _P, _F, _P, _SZ, _P, _INT, _P]),
+    "wq_read_probe": (_INT, [_P, _SZ, _P, _INT, _P]),
 }
 
 
@@ -324,3 +325,14 @@ def qlinear_run(fmt, x, w, scale=None, global_scale=1.0, N=None, path="auto", ou
                            0 if ws is None else ws.numel(), _ptr(out), _PATHS[path], _stream(dev))
     _check("qlinear_run", rc)
     return out
+
+
+def wq_read_probe(src, sink, nbytes=None, grid=None):
+    """Streaming read of nbytes (default: all) of the device tensor src; sink: int32 tensor of >= grid words."""
+    dev = src.device
+    nbytes = src.numel() * src.element_size() if nbytes is None else nbytes
+    grid = sink.numel() if grid is None else grid
+    _need(sink, "sink", torch.int32, dev)
+    if grid > sink.numel() or nbytes > src.numel() * src.element_size():
+        raise ValueError("grid exceeds sink or nbytes exceeds src")
+    _check("wq_read_probe", lib().wq_read_probe(_ptr(src), nbytes, _ptr(sink), grid, _stream(dev)))

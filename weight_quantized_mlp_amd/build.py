@@ -12,7 +12,7 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
-SOURCES = ["abi.cpp", "gemv.hip", "gemv_fast.hip", "mfma.hip", "moe.hip", "pack.hip"]
+SOURCES = ["abi.cpp", "gemv.hip", "gemv_fast.hip", "mfma.hip", "moe.hip", "pack.hip", "probe.hip"]
 LIB = os.path.join(HERE, "libwqmlp.so")
 ARCH = "gfx950"
 FLAGS = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",

@@ -461,6 +461,15 @@ int awq_dequant_f16(int64_t E, int64_t N, int64_t K, const void* bank, int meta_
                                          reinterpret_cast<hipStream_t>(stream)));
 }
 
+int wq_read_probe(const void* src, size_t bytes, uint32_t* sink, int grid, void* stream) {
+  if (src == nullptr || sink == nullptr || bytes == 0 || bytes % 16 || grid < 1 || grid > (1 << 20)) return WQ_EINVAL;
+  if (!all_aligned({src, sink})) return WQ_EALIGN;
+  if (any_overlap({{sink, (size_t)grid * 4}}, {{src, bytes}})) return WQ_EOVERLAP;
+  const int rc = check_device({src, sink});
+  if (rc != WQ_OK) return rc;
+  return launched(wq::launch_read_probe(src, bytes, sink, grid, reinterpret_cast<hipStream_t>(stream)));
+}
+
 size_t qlinear_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K, int flags) {
   if ((fmt != WQ_FMT_FP8W && fmt != WQ_FMT_NVFP4) || flags < WQ_PATH_AUTO || flags > WQ_PATH_MFMA) return 0;
   if (M <= 0 || N <= 0 || K <= 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim || !elems_ok(M, N, K)) return 0;

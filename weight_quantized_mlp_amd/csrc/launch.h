@@ -95,6 +95,11 @@ hipError_t launch_nvfp4_dequant(int64_t N, int64_t K, const uint8_t* blk, float 
 hipError_t launch_awq_dequant(int64_t E, int64_t N, int64_t K, const uint8_t* bank, int meta_layout,
                               uint16_t* out, hipStream_t st);
 
+// ---- measurement helper ---------------------------------------------------------------------
+// Streaming read of `bytes` (a multiple of 16) at src by `grid` workgroups of 256 threads; sink holds
+// grid 32-bit words (written only when a lane's XOR fold equals one fixed value).
+hipError_t launch_read_probe(const void* src, size_t bytes, uint32_t* sink, int grid, hipStream_t st);
+
 // ---- AWQ bank geometry (shared by the packer, the decoder and the step) ------------------------
 struct AwqLayout {
   int64_t G;           // groups of 32 per row
