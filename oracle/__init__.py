@@ -18,6 +18,8 @@ cites the page and section it follows:
   as implemented" -- the three-level NVFP4 tensor and the 36-byte record.
 * "[Kernel][SM70] Add native-g32 AWQ QPN M1 operator", section "What it
   does" -- the AWQ int4 group-32 routed-expert single-token step.
+* "Qwen3.8-27B-NVFP4", section "Implemented execution path" -- the per-token
+  8-bit activation quantization of the W4A8 variant (actquant.py).
 
 Pins (what ties each function to something other than itself) are in
 ``tests/test_oracle.py``.  Parity unpinned: the full-size MLP results at the
@@ -29,7 +31,8 @@ from .dequant import (fp8w_dequant, nvfp4_dequant, nvfp4_dequant_parts, awq_dequ
                       awq_dequant_bias, awq_bias_bits)
 from .pack import (block64_pack, block64_unpack, awq_bank_layout, awq_pack_bank,
                    awq_unpack_bank)
-from .mlp import silu, swiglu_mlp, mlp_fp8w_ref, mlp_nvfp4_ref, mlp_bruteforce
+from .mlp import silu, swiglu_mlp, mlp_fp8w_ref, mlp_nvfp4_ref, mlp_nvfp4_w4a8_ref, mlp_bruteforce
+from .actquant import token_exponent, e4m3_encode_rne, quant_e4m3_per_token
 from .moe import moe_awq_m1_ref, moe_w13_stage_ref, moe_w2_stage_ref, moe_bruteforce
 from .metric import normwise_rel_err
 

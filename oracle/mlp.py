@@ -74,6 +74,37 @@ def mlp_nvfp4_ref(x, gblk, ggs, ublk, ugs, dblk, dgs, return_act=False, rows_blo
     return (out, act) if return_act else out
 
 
+def mlp_nvfp4_w4a8_ref(x, gblk, ggs, ublk, ugs, dblk, dgs, stages=False):
+    """The W4A8 variant of the NVFP4 MLP: the same definition with both linears' activations quantized per
+    token to E4M3 (page "Qwen3.8-27B-NVFP4", section "Implemented execution path": per-token dynamic
+    activation quantization, one quantization of x shared by gate and up; the down projection's input
+    act is quantized the same way).
+
+        xq, sx = quant(x);     xd = e4m3(xq) * sx                 (exact)
+        act    = silu(xd Wg^T) * (xd Wu^T)                        (float64)
+        act32  = RN_f32(act)   -- the quantization decision is taken on the float32 act, the precision in
+                                  which the device holds act (reading: the page gives no precision for it)
+        aq, sa = quant(act32); out = (e4m3(aq) * sa) Wd^T         (float64)
+
+    With stages=True returns (out, dict(xq, sx, act32, aq, sa)).
+    """
+    from .actquant import quant_e4m3_per_token
+    xq, sx = quant_e4m3_per_token(x)
+    xd = e4m3_to_f64(xq) * sx[:, None]
+    Wg = nvfp4_weight_f64(gblk, ggs)
+    Wu = nvfp4_weight_f64(ublk, ugs)
+    g = xd @ Wg.T
+    u = xd @ Wu.T
+    del Wg, Wu
+    act32 = (silu(g) * u).astype(np.float32)
+    aq, sa = quant_e4m3_per_token(act32.astype(np.float64))
+    ad = e4m3_to_f64(aq) * sa[:, None]
+    out = ad @ nvfp4_weight_f64(dblk, dgs).T
+    if stages:
+        return out, dict(xq=xq, sx=sx, act32=act32, aq=aq, sa=sa)
+    return out
+
+
 def mlp_bruteforce(x, Wg, Wu, Wd):
     """Pure-Python triple loop of the same definition, for tiny shapes only.
 

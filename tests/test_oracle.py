@@ -355,6 +355,147 @@ def test_moe_special_cases():
     assert np.array_equal(out, (codecs.f16_bits_to_f64(y[0]) * 0.75).astype(np.float16).view(np.uint16))
 
 
+# ---- per-token E4M3 activation quantization (W4A8 variant) --------------------------------------------
+def torch_e4m3_encode(v32):
+    """Library encode: float32 -> float8_e4m3fn (round to nearest even) -> code bytes."""
+    return torch.from_numpy(np.ascontiguousarray(v32, dtype=np.float32)).to(torch.float8_e4m3fn) \
+        .view(torch.uint8).numpy()
+
+
+def e4m3_encode_cases():
+    vals = codecs.e4m3_to_f64(np.arange(0x7F))                         # every non-negative finite value
+    mids = (vals[:-1] + vals[1:]) / 2                                 # every exact tie between neighbours
+    r = np.random.default_rng(17)
+    rnd = np.concatenate([r.standard_normal(4000) * 10 ** r.uniform(-4, 2.6, 4000),
+                          r.uniform(-448, 448, 2000), r.uniform(-2 ** -8, 2 ** -8, 2000)])
+    v = np.concatenate([vals, -vals, mids, -mids, rnd, [0.0, -0.0, 448.0, -448.0, 2 ** -10, 3 * 2 ** -11]])
+    v = v[np.abs(v) <= 448].astype(np.float32).astype(np.float64)     # float32-exact, within range
+    return v
+
+
+def test_e4m3_encode_matches_torch_cast():
+    v = e4m3_encode_cases()
+    assert np.array_equal(oracle.e4m3_encode_rne(v), torch_e4m3_encode(v))
+
+
+def test_e4m3_encode_matches_pure_python_nearest_search():
+    # independent of the value table and searchsorted: scan the 254 finite codes decoded from their fields
+    table = [(float(codecs.e4m3_fields_to_f64(c)), c) for c in range(256) if c not in (0x7F, 0xFF)]
+    r = np.random.default_rng(3)
+    v = np.concatenate([e4m3_encode_cases()[::23], r.uniform(-448, 448, 300)])
+    for x in v:
+        best = None
+        for val, c in table:
+            if math.copysign(1.0, val) != math.copysign(1.0, x):   # same sign side (zero keeps x's sign)
+                continue
+            key = (abs(val - x), c & 1)                              # nearest, then the even code
+            if best is None or key < best[0]:
+                best = (key, c)
+        assert oracle.e4m3_encode_rne(np.array([x]))[0] == best[1], x
+
+
+def test_token_exponent_lands_the_row_max_in_224_448():
+    assert oracle.token_exponent(448.0) == 0 and oracle.token_exponent(224.0) == -1
+    assert oracle.token_exponent(np.nextafter(448.0, 1e9)) == 1
+    assert oracle.token_exponent(np.nextafter(224.0, 1e9)) == 0
+    assert oracle.token_exponent(0.0) == 0
+    r = np.random.default_rng(8)
+    for a in np.concatenate([10 ** r.uniform(-30, 30, 2000), 448.0 * 2.0 ** np.arange(-40, 40)]):
+        e = oracle.token_exponent(a)
+        assert 224.0 < a * 2.0 ** -e <= 448.0, a
+
+
+def test_quant_per_token_rows():
+    r = np.random.default_rng(4)
+    x = r.standard_normal((5, 96)) * np.array([[1e-3], [1.0], [30.0], [1e5], [0.0]])
+    codes, scale = oracle.quant_e4m3_per_token(x)
+    assert scale[4] == 1.0 and np.all(codes[4] & 0x7F == 0)             # a row of (signed) zeros
+    assert np.array_equal(codes[4] >> 7, np.signbit(x[4]).astype(np.uint8))
+    for m in range(4):
+        e = int(round(math.log2(scale[m])))
+        assert scale[m] == 2.0 ** e and 224 < np.max(np.abs(x[m])) / scale[m] <= 448
+        xs = np.ldexp(x[m], -e)
+        x32 = xs.astype(np.float32)
+        exact = x32.astype(np.float64) == xs                               # where float32 holds the value
+        assert np.array_equal(codes[m][exact], torch_e4m3_encode(x32)[exact])
+        # the row max maps onto the top binade's codes, and dequantisation stays within half a code step
+        deq = codecs.e4m3_to_f64(codes[m]) * scale[m]
+        assert np.all(np.abs(deq - x[m]) <= np.maximum(np.abs(x[m]) * 2.0 ** -4, 2.0 ** -10 * scale[m]))
+
+
+def test_w4a8_mlp_matches_pure_python_bruteforce():
+    # the whole W4A8 definition in plain Python: quantize x per row (nearest-code scan), dequantize, triple
+    # loops, silu, act rounded to float32, quantize act per row, dequantize, down projection
+    H, I = 64, 64
+    W = {n: synth.nvfp4_tensor(*shp, 3, t) for n, t, shp in (("g", 1, (I, H)), ("u", 2, (I, H)), ("d", 3, (H, I)))}
+    xb, _ = synth.nvfp4_x(3, H, outlier_frac=0.34)
+    x = codecs.bf16_bits_to_f64(xb)
+    blk = {n: pack.block64_pack(*W[n][:2]) for n in W}
+    ref = mlp.mlp_nvfp4_w4a8_ref(x, blk["g"], W["g"][2], blk["u"], W["u"][2], blk["d"], W["d"][2])
+    table = [(float(codecs.e4m3_fields_to_f64(c)), c) for c in range(256) if c not in (0x7F, 0xFF)]
+
+    def q_row(row):
+        amax = max(abs(v) for v in row)
+        e = 0
+        if amax > 0:
+            while amax > 448.0 * 2.0 ** e:
+                e += 1
+            while amax <= 448.0 * 2.0 ** (e - 1):
+                e -= 1
+        out = []
+        for v in row:
+            t = v * 2.0 ** -e
+            best = min((abs(val - t), c & 1, val) for val, c in table if math.copysign(1, val) == math.copysign(1, t))
+            out.append(best[2] * 2.0 ** e)
+        return out
+
+    table16 = np.array(OCP_E2M1 + [-v for v in OCP_E2M1])
+
+    def wt(wp, ws, gs):
+        nib = np.stack([wp & 15, wp >> 4], axis=-1).reshape(wp.shape[0], -1)
+        inv = float(np.float32(1.0) / np.float32(gs))
+        return (table16[nib] * np.repeat(torch_e4m3(ws).astype(np.float64), 16, axis=1) * inv).tolist()
+
+    Wg, Wu, Wd = wt(*W["g"]), wt(*W["u"]), wt(*W["d"])
+    for m in range(3):
+        xr = q_row(list(x[m]))
+        act = []
+        for i in range(I):
+            g = sum(xr[k] * Wg[i][k] for k in range(H))
+            u = sum(xr[k] * Wu[i][k] for k in range(H))
+            sg = g / (1.0 + math.exp(-g)) if g >= 0 else g * math.exp(g) / (1.0 + math.exp(g))
+            act.append(float(np.float32(sg * u)))
+        ar = q_row(act)
+        o = [sum(ar[q] * Wd[j][q] for q in range(I)) for j in range(H)]
+        err, scale = oracle.normwise_rel_err(ref[m], np.array(o))
+        assert scale > 1e-6 and err < 1e-12, (m, err)
+
+
+def test_w4a8_pins_catch_planted_mistakes(monkeypatch):
+    from oracle import actquant
+    v = e4m3_encode_cases()
+    good = torch_e4m3_encode(v)
+    # ties away from zero instead of to the even code
+    pos = actquant._POS_VALUES
+
+    def away(x):
+        x = np.asarray(x, dtype=np.float64)
+        a = np.abs(x)
+        hi = np.minimum(np.searchsorted(pos, a), pos.size - 1)
+        lo = np.maximum(hi - 1, 0)
+        c = np.where(pos[hi] - a <= a - pos[lo], hi, lo).astype(np.uint8)
+        return np.where(np.signbit(x), c | 0x80, c).astype(np.uint8)
+    assert not np.array_equal(away(v), good)
+    # truncation instead of rounding
+    trunc = np.where(np.signbit(v), 0x80, 0) | (np.searchsorted(pos, np.abs(v), side="right") - 1)
+    assert not np.array_equal(trunc.astype(np.uint8), good)
+    # a scale that puts the row max at 448 exactly (amax / 448, not a power of two) changes the codes
+    x = np.random.default_rng(5).standard_normal((1, 256)) * 3.0
+    c_pow2, _ = oracle.quant_e4m3_per_token(x)
+    c_div = torch_e4m3_encode((x[0] / (np.max(np.abs(x)) / 448.0)).astype(np.float32))
+    assert not np.array_equal(c_pow2[0], c_div)
+
+
 # ---- the parity metric ---------------------------------------------------------------------------------
 # Hand-computed cases of the row-normwise error  max_m ( max_o |y - r| / max_o |r| ), with the row scale
 # min_m max_o |r| returned beside it.  Each tuple: (y, ref, expected error, expected min row scale).
