@@ -309,18 +309,18 @@ def nvfp4_weights(torch, wq, w, dev):
     return blk, gs
 
 
-def nvfp4_run(torch, wq, synth, blk, gs, M, K, S, copies, outlier):
+def nvfp4_run(torch, wq, synth, blk, gs, M, K, S, copies, outlier, act=None):
     dev = torch.device("cuda:0")
     sets = [blk] + [{n: t.clone() for n, t in blk.items()} for _ in range(copies - 1)]
     xb, _ = synth.nvfp4_x(M, outlier_frac=outlier)
     x = torch.from_numpy(xb.view("int16")).to(dev).view(torch.bfloat16)
     out = torch.empty((M, H), dtype=torch.float32, device=dev)
-    ws = torch.empty(wq.mlp_workspace_bytes(wq.WQ_FMT_NVFP4, M, H, I), dtype=torch.uint8, device=dev)
+    ws = torch.empty(wq.mlp_workspace_bytes(wq.WQ_FMT_NVFP4, M, H, I, "auto", act), dtype=torch.uint8, device=dev)
 
     def step(i, stage=None):
         b = sets[i % copies]
         wq.mlp_nvfp4_run(x, b["gate"], gs["gate"], b["up"], gs["up"], b["down"], gs["down"], out=out, workspace=ws,
-                         stage=stage)
+                         stage=stage, act=act)
 
     step(0)
     torch.cuda.synchronize()
@@ -604,7 +604,8 @@ def main():
     extras = {}
     want = set() if args.extras == "none" else (
         {"fp8_tiny", "nvfp4_decode", "nvfp4_prefill_512", "nvfp4_prefill_8192", "nvfp4_batch8", "fp8_batch8",
-         "fp8_prefill_512", "awq", "awq4", "read_ceiling"} if args.extras == "all"
+         "fp8_prefill_512", "nvfp4_w4a8_prefill_512", "nvfp4_w4a8_prefill_8192", "awq", "awq4", "read_ceiling"}
+        if args.extras == "all"
         else set(args.extras.split(",")))
     if "fp8_tiny" in want:
         extras["fp8_tiny_256x512"] = fp8_tiny(torch, wq, synth, K, S)
@@ -621,7 +622,8 @@ def main():
             gateup_us=round(n["gu"].med * 1e6, 2), down_us=round(n["dn"].med * 1e6, 2), path="mfma",
             weight_copies=copies, step=n["full"].summary())
         log(key, extras[key])
-    if want & {"nvfp4_decode", "nvfp4_prefill_512", "nvfp4_prefill_8192", "nvfp4_batch8"}:
+    if want & {"nvfp4_decode", "nvfp4_prefill_512", "nvfp4_prefill_8192", "nvfp4_batch8", "nvfp4_w4a8_prefill_512",
+               "nvfp4_w4a8_prefill_8192"}:
         data["nvfp4_w"] = synth.nvfp4_mlp_weights()
         blk, gs = nvfp4_weights(torch, wq, data["nvfp4_w"], dev)
         if "nvfp4_decode" in want:
@@ -640,10 +642,12 @@ def main():
                 gateup_us=round(n["gu"].med * 1e6, 2), down_us=round(n["dn"].med * 1e6, 2), path="mfma",
                 weight_copies=n["copies"], step=n["full"].summary())
             log("nvfp4_batch8", extras["nvfp4_batch8"])
-        for M, key, steps in ((512, "nvfp4_prefill_512", 60), (8192, "nvfp4_prefill_8192", 12)):
+        for M, key, steps, act in ((512, "nvfp4_prefill_512", 60, None), (8192, "nvfp4_prefill_8192", 12, None),
+                                   (512, "nvfp4_w4a8_prefill_512", 60, "e4m3"),
+                                   (8192, "nvfp4_w4a8_prefill_8192", 12, "e4m3")):
             if key not in want:
                 continue
-            n = nvfp4_run(torch, wq, synth, blk, gs, M, steps, S, 2, 0.01)
+            n = nvfp4_run(torch, wq, synth, blk, gs, M, steps, S, 2, 0.01, act)
             tm = n["full"].med
             tfl = 2.0 * M * 3 * H * I / tm / 1e12
             gu_ms, dn_ms = n["gu"].med * 1e3, n["dn"].med * 1e3

@@ -111,32 +111,38 @@ def test_fp8_linear_reads_every_code(path, xdt, K):
         check_columns(y1, dq, [k], f"fp8 {path} {xdt} K={K} M=1")
 
 
-NV_LINEAR = ([("gemv", x, K) for x in ("f32", "bf16", "f16") for K in (192, 512)]
-             + [("mfma", x, K) for x in ("f32", "bf16") for K in (192, 512)])
+# (path, x dtype, K, activation variant); the W4A8 variant (act "e4m3") quantizes the one-hot rows to E4M3
+# (1.0 -> code 256 under the row scale 2^-8, exactly) and runs its E4M3 MFMAs on the decoded weights
+NV_LINEAR = ([("gemv", x, K, None) for x in ("f32", "bf16", "f16") for K in (192, 512)]
+             + [("mfma", x, K, None) for x in ("f32", "bf16") for K in (192, 512)]
+             + [("mfma", x, K, "e4m3") for x in ("f32", "bf16") for K in (384, 512)])
 
 
-@pytest.mark.parametrize("path,xdt,K", NV_LINEAR)
-def test_nvfp4_linear_reads_every_code_under_every_scale(path, xdt, K):
+@pytest.mark.parametrize("path,xdt,K,act", NV_LINEAR)
+def test_nvfp4_linear_reads_every_code_under_every_scale(path, xdt, K, act):
     N = 256
     blk, gs = nvfp4_matrix(N, K, 200 + K, 448 * 6 / 0.3)
     dq = oracle.nvfp4_dequant(blk, gs)
     hot = nvfp4_hot(K)
     x = one_hot(len(hot), K, hot)
-    y = host(wq.qlinear_run(wq.WQ_FMT_NVFP4, dev(x).to(TORCH_X[xdt]), dev(blk), None, float(gs), path=path))
-    check_columns(y, dq, hot, f"nvfp4 {path} {xdt} K={K}")
+    y = host(wq.qlinear_run(wq.WQ_FMT_NVFP4, dev(x).to(TORCH_X[xdt]), dev(blk), None, float(gs), path=path, act=act))
+    check_columns(y, dq, hot, f"nvfp4 {path} {xdt} K={K} act={act}")
     for k in (hot[0], hot[37], hot[-1]):
         y1 = host(wq.qlinear_run(wq.WQ_FMT_NVFP4, dev(one_hot(1, K, [k])).to(TORCH_X[xdt]), dev(blk), None,
-                                 float(gs), path=path))
-        check_columns(y1, dq, [k], f"nvfp4 {path} {xdt} K={K} M=1")
+                                 float(gs), path=path, act=act))
+        check_columns(y1, dq, [k], f"nvfp4 {path} {xdt} K={K} act={act} M=1")
 
 
 # ---- gate/up projection ------------------------------------------------------------------------------------
-H, I = 512, 320          # gate/up [I, H]: rows 0..255 exhaustive, 256..319 random finite codes
+H, I = 512, 384          # gate/up [I, H]: rows 0..255 exhaustive, 256..383 random finite codes (both dimensions
+                         # multiples of 128, as the W4A8 variant needs)
 
 
 def act_view(ws, fmt, path, M):
     """act as the gate/up stage leaves it in the workspace (the header's layout)."""
-    if path == "gemv":
+    if fmt == "nvfp4w8":                            # W4A8: x codes, x scales, then act float32
+        off, n, dt = a256(M * H) + a256(M * 4), M * I * 4, np.float32
+    elif path == "gemv":
         off, n, dt = 0, M * I * (4 if fmt == "fp8" else 2), (np.float32 if fmt == "fp8" else np.float16)
     elif fmt == "fp8":
         off, n, dt = a256(M * H * 2) + a256(M * 4) + a256(M * I * 2), M * I * 4, np.float32
@@ -158,10 +164,11 @@ def gateup(fmt, path, xdt, x, gate, up, M):
     else:
         (bg, gg), (bu, gu) = gate, up
         bd = np.zeros((H, I // 64, 36), np.uint8)
-        nb = wq.mlp_workspace_bytes(wq.WQ_FMT_NVFP4, M, H, I, path)
+        act = "e4m3" if fmt == "nvfp4w8" else None
+        nb = wq.mlp_workspace_bytes(wq.WQ_FMT_NVFP4, M, H, I, path, act)
         ws = torch.zeros(nb, dtype=torch.uint8, device=xt.device)
         wq.mlp_nvfp4_run(xt, dev(bg), float(gg), dev(bu), float(gu), dev(bd), 1.0, workspace=ws, path=path,
-                         stage="gateup")
+                         stage="gateup", act=act)
     torch.cuda.synchronize()
     return act_view(ws, fmt, path, M).astype(np.float64)
 
@@ -194,8 +201,9 @@ def exhaustive_rows(w, s):
     return wf, sf
 
 
-GATEUP = [(f, p, x, M) for f in ("fp8", "nvfp4") for p in ("gemv", "mfma") for x in ("f32", "bf16")
-          for M in (1, 20)]
+GATEUP = ([(f, p, x, M) for f in ("fp8", "nvfp4") for p in ("gemv", "mfma") for x in ("f32", "bf16")
+           for M in (1, 20)]
+          + [("nvfp4w8", "mfma", x, M) for x in ("f32", "bf16") for M in (1, 20)])
 
 
 @pytest.mark.parametrize("fmt,path,xdt,M", GATEUP)
@@ -224,7 +232,7 @@ def test_gateup_reads_every_code(fmt, path, xdt, M):
     # up exhaustive, gate 128: act = 128 * dq(up) exactly (float16-rounded once for NVFP4)
     act = gateup(fmt, path, xdt, x, const128, ex, M)
     want = np.stack([128.0 * dq[:, k] for k in hot])
-    if fmt == "nvfp4":
+    if fmt == "nvfp4":                              # float16 act; W4A8 keeps act in float32
         want = want.astype(np.float16).astype(np.float64)
     ok = (act == want) | (np.isnan(act) & np.isnan(want))
     assert ok.all(), f"{fmt} {path} {xdt} M={M}: up read-out differs at {np.argwhere(~ok)[:6].tolist()}"
@@ -232,7 +240,7 @@ def test_gateup_reads_every_code(fmt, path, xdt, M):
     act = gateup(fmt, path, xdt, x, ex, const1, M)
     g = np.stack([dq[:, k] for k in hot])
     want = oracle.silu(np.nan_to_num(g)) * np.where(np.isnan(g), np.nan, 1.0)
-    if fmt == "fp8":
+    if fmt in ("fp8", "nvfp4w8"):
         tol = 8 * np.spacing(np.abs(want).astype(np.float32)).astype(np.float64) + 1e-38
     else:
         w16 = want.astype(np.float16)

@@ -15,7 +15,8 @@ import torch
 
 __all__ = [
     "WQError", "lib", "lib_path", "WQ_F32", "WQ_BF16", "WQ_F16", "WQ_FMT_FP8W", "WQ_FMT_NVFP4",
-    "WQ_PATH_AUTO", "WQ_PATH_GEMV", "WQ_PATH_MFMA", "WQ_STAGE_GATEUP_ONLY", "WQ_STAGE_DOWN_ONLY", "wq_abi_version", "wq_strerror",
+    "WQ_PATH_AUTO", "WQ_PATH_GEMV", "WQ_PATH_MFMA", "WQ_STAGE_GATEUP_ONLY", "WQ_STAGE_DOWN_ONLY", "WQ_ACT_E4M3",
+    "wq_abi_version", "wq_strerror",
     "WQ_STATIC_SCRATCH_BYTES", "mlp_workspace_bytes", "mlp_fp8w_run", "mlp_fp8w_run_noalloc", "mlp_nvfp4_run", "awq_bank_bytes", "moe_awq_m1_run",
     "nvfp4_pack_block64", "awq_pack_bank", "fp8w_dequant_f32", "nvfp4_dequant_f32", "awq_dequant_f16",
     "qlinear_workspace_bytes", "qlinear_run", "wq_read_probe",
@@ -25,9 +26,11 @@ WQ_F32, WQ_BF16, WQ_F16 = 0, 1, 2
 WQ_FMT_FP8W, WQ_FMT_NVFP4 = 0, 1
 WQ_PATH_AUTO, WQ_PATH_GEMV, WQ_PATH_MFMA = 0, 1, 2
 WQ_STAGE_GATEUP_ONLY, WQ_STAGE_DOWN_ONLY = 4, 8
+WQ_ACT_E4M3 = 16
 WQ_STATIC_SCRATCH_BYTES = 32 << 20
 _PATHS = {"auto": WQ_PATH_AUTO, "gemv": WQ_PATH_GEMV, "mfma": WQ_PATH_MFMA}
 _STAGES = {None: 0, "gateup": WQ_STAGE_GATEUP_ONLY, "down": WQ_STAGE_DOWN_ONLY}
+_ACTS = {None: 0, "e4m3": WQ_ACT_E4M3}
 
 lib_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libwqmlp.so")
 _lib = None
@@ -128,8 +131,8 @@ def wq_strerror(rc):
     return lib().wq_strerror(rc).decode()
 
 
-def mlp_workspace_bytes(fmt, M, H, I, path="auto"):
-    return lib().mlp_workspace_bytes(fmt, M, H, I, _PATHS[path])
+def mlp_workspace_bytes(fmt, M, H, I, path="auto", act=None):
+    return lib().mlp_workspace_bytes(fmt, M, H, I, _PATHS[path] | _ACTS[act])
 
 
 def _workspace(nbytes, dev, workspace):
@@ -192,8 +195,9 @@ def mlp_fp8w_run_noalloc(x, w_gate, s_gate, w_up, s_up, w_down, s_down, out, pat
 
 
 def mlp_nvfp4_run(x, gate_blk, gate_gs, up_blk, up_gs, down_blk, down_gs, out=None, workspace=None, path="auto",
-                  stage=None):
-    """NVFP4 Block64 SwiGLU MLP.  x [M,H]; gate/up_blk [I,H/64,36] u8; down_blk [H,I/64,36] u8; gs floats."""
+                  stage=None, act=None):
+    """NVFP4 Block64 SwiGLU MLP.  x [M,H]; gate/up_blk [I,H/64,36] u8; down_blk [H,I/64,36] u8; gs floats.
+    act="e4m3": the W4A8 variant (activations quantized per row to E4M3; MFMA path)."""
     sflags = _stage_flags(stage, workspace)
     dev = x.device
     M, H = x.shape
@@ -205,11 +209,11 @@ def mlp_nvfp4_run(x, gate_blk, gate_gs, up_blk, up_gs, down_blk, down_gs, out=No
     if out is None:
         out = torch.empty((M, H), dtype=torch.float32, device=dev)
     _need(out, "out", torch.float32, dev, M * H)
-    nb = mlp_workspace_bytes(WQ_FMT_NVFP4, M, H, I, path)
+    nb = mlp_workspace_bytes(WQ_FMT_NVFP4, M, H, I, path, act)
     ws = _workspace(nb, dev, workspace)
     rc = lib().mlp_nvfp4_run(M, H, I, _ptr(x), _xdtype(x), _ptr(gate_blk), float(gate_gs), _ptr(up_blk),
                              float(up_gs), _ptr(down_blk), float(down_gs), _ptr(ws), ws.numel(), _ptr(out),
-                             _PATHS[path] | sflags, _stream(dev))
+                             _PATHS[path] | sflags | _ACTS[act], _stream(dev))
     _check("mlp_nvfp4_run", rc)
     return out
 
@@ -303,12 +307,13 @@ def awq_dequant_f16(bank, E, N, K, meta_layout=3):
     return out
 
 
-def qlinear_workspace_bytes(fmt, M, N, K, path="auto"):
-    return lib().qlinear_workspace_bytes(fmt, M, N, K, _PATHS[path])
+def qlinear_workspace_bytes(fmt, M, N, K, path="auto", act=None):
+    return lib().qlinear_workspace_bytes(fmt, M, N, K, _PATHS[path] | _ACTS[act])
 
 
-def qlinear_run(fmt, x, w, scale=None, global_scale=1.0, N=None, path="auto", out=None, workspace=None):
-    """y = x dq(W)^T.  FP8: w [N,K] u8 + scale [N] f32; NVFP4: w Block64 [N,K/64,36] + global_scale."""
+def qlinear_run(fmt, x, w, scale=None, global_scale=1.0, N=None, path="auto", out=None, workspace=None, act=None):
+    """y = x dq(W)^T.  FP8: w [N,K] u8 + scale [N] f32; NVFP4: w Block64 [N,K/64,36] + global_scale.
+    act="e4m3" (NVFP4): x quantized per row to E4M3 first (the W4A8 variant; MFMA path)."""
     dev = x.device
     M, K = x.shape
     N = w.shape[0] if N is None else N
@@ -319,10 +324,10 @@ def qlinear_run(fmt, x, w, scale=None, global_scale=1.0, N=None, path="auto", ou
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=dev)
     _need(out, "out", torch.float32, dev, M * N)
-    nb = 0 if x.dtype == torch.float16 else qlinear_workspace_bytes(fmt, M, N, K, path)
+    nb = 0 if x.dtype == torch.float16 else qlinear_workspace_bytes(fmt, M, N, K, path, act)
     ws = _workspace(nb, dev, workspace) if nb else None
     rc = lib().qlinear_run(fmt, M, N, K, _ptr(x), _xdtype(x, allow_f16=True), _ptr(w), _ptr(scale), float(global_scale), _ptr(ws),
-                           0 if ws is None else ws.numel(), _ptr(out), _PATHS[path], _stream(dev))
+                           0 if ws is None else ws.numel(), _ptr(out), _PATHS[path] | _ACTS[act], _stream(dev))
     _check("qlinear_run", rc)
     return out
 

@@ -136,12 +136,17 @@ int pick_path(int fmt, int64_t M, int64_t D0, int64_t D1, size_t wb, int flags) 
   if (M >= narrow && wb >= (size_t)WQ_NARROW_MIN_WEIGHT_BYTES && D0 % 64 == 0 && D1 % 64 == 0) return WQ_PATH_MFMA;
   return WQ_PATH_GEMV;
 }
+// The W4A8 variant (WQ_ACT_E4M3) runs on the MFMA path only.
 int mlp_path(int fmt, int64_t M, int64_t H, int64_t I, int flags) {
+  if (flags & WQ_ACT_E4M3) return WQ_PATH_MFMA;
   return pick_path(fmt, M, H, I, 2 * wbytes(fmt, I, H) + wbytes(fmt, H, I), flags);
 }
 int linear_path(int fmt, int64_t M, int64_t N, int64_t K, int flags) {
+  if (flags & WQ_ACT_E4M3) return WQ_PATH_MFMA;
   return pick_path(fmt, M, N, K, wbytes(fmt, N, K), flags);
 }
+// A dimension the W4A8 GEMM takes as K: whole 128-wide steps, at least two.
+bool w8_k_ok(int64_t K) { return K % 128 == 0 && K >= 256; }
 
 // Split-K scratch of the MFMA path: gate+up and down run one after the other and share it.
 size_t mlp_partials(int fmt, int64_t M, int64_t H, int64_t I) {
@@ -182,9 +187,36 @@ MfmaWs mfma_ws(int fmt, int64_t M, int64_t H, int64_t I) {
   return w;
 }
 
+// Workspace regions of the W4A8 variant (each 256-byte aligned, in this order): xq [M,H] E4M3 codes of x,
+// sx [M] float32 (x row scales), act32 [M,I] float32, aq [M,I] E4M3 codes of act, sa [M] float32 (act row
+// scales), then the split-K partial tiles of the larger of the two GEMMs.
+struct W8Ws {
+  size_t xq, sx, act32, aq, sa, partials, total;
+};
+W8Ws w8_ws(int64_t M, int64_t H, int64_t I) {
+  W8Ws w{};
+  size_t o = 0;
+  w.xq = o;
+  o += align256((size_t)M * H);
+  w.sx = o;
+  o += align256((size_t)M * 4);
+  w.act32 = o;
+  o += align256((size_t)M * I * 4);
+  w.aq = o;
+  o += align256((size_t)M * I);
+  w.sa = o;
+  o += align256((size_t)M * 4);
+  w.partials = o;
+  o += align256(std::max(wq::w4a8_partial_bytes((int)M, (int)H, (int)I, true),
+                         wq::w4a8_partial_bytes((int)M, (int)I, (int)H, false)));
+  w.total = o;
+  return w;
+}
+
 // Workspace of the two-layer MLP; 0 means "invalid".
 size_t mlp_ws(int fmt, int64_t M, int64_t H, int64_t I, int flags) {
   if (M <= 0 || H <= 0 || I <= 0 || M > kMaxDim || H > kMaxDim || I > kMaxDim || !elems_ok(M, H, I)) return 0;
+  if (flags & WQ_ACT_E4M3) return fmt == WQ_FMT_NVFP4 && w8_k_ok(H) && w8_k_ok(I) ? w8_ws(M, H, I).total : 0;
   if (mlp_path(fmt, M, H, I, flags) == WQ_PATH_GEMV) return align256((size_t)M * I * act_gemv_bytes(fmt));
   return mfma_ws(fmt, M, H, I).total;
 }
@@ -237,13 +269,16 @@ int mlp_run(int fmt, int64_t M, int64_t H, int64_t I, const void* x, int x_dtype
             const float* sd, float gd, void* ws, size_t ws_bytes, float* out, int flags, void* stream,
             bool use_static = false) {
   const int stage = flags & (WQ_STAGE_GATEUP_ONLY | WQ_STAGE_DOWN_ONLY);
-  if ((flags & ~15) || (flags & 3) == 3 || stage == (WQ_STAGE_GATEUP_ONLY | WQ_STAGE_DOWN_ONLY)) return WQ_EINVAL;
+  if ((flags & ~31) || (flags & 3) == 3 || stage == (WQ_STAGE_GATEUP_ONLY | WQ_STAGE_DOWN_ONLY)) return WQ_EINVAL;
+  const bool w8 = (flags & WQ_ACT_E4M3) != 0;   // W4A8: NVFP4 only, MFMA path only
+  if (w8 && (fmt != WQ_FMT_NVFP4 || (flags & 3) == WQ_PATH_GEMV)) return WQ_EINVAL;
   const bool do_gu = stage != WQ_STAGE_DOWN_ONLY, do_down = stage != WQ_STAGE_GATEUP_ONLY;
   if (x_dtype != WQ_F32 && x_dtype != WQ_BF16) return WQ_EINVAL;
   if (M < 0 || M > kMaxDim) return WQ_EINVAL;
   if (H <= 0 || I <= 0 || H > kMaxDim || I > kMaxDim || !elems_ok(M, H, I)) return WQ_EINVAL;
   const int path = mlp_path(fmt, M, H, I, flags);
   if (!shape_ok(fmt, path, H, I, x_dtype)) return WQ_EINVAL;
+  if (w8 && (!w8_k_ok(H) || !w8_k_ok(I))) return WQ_EINVAL;
   if (any_null({wg, wu, wd})) return WQ_EINVAL;
   if (fmt == WQ_FMT_FP8W && any_null({sg, su, sd})) return WQ_EINVAL;
   if (fmt == WQ_FMT_NVFP4) {
@@ -255,7 +290,7 @@ int mlp_run(int fmt, int64_t M, int64_t H, int64_t I, const void* x, int x_dtype
   if (use_static) ws = nullptr;
   if (!all_aligned({x, wg, wu, wd, out, ws})) return WQ_EALIGN;
   if (fmt == WQ_FMT_FP8W && !all_aligned({sg, su, sd})) return WQ_EALIGN;
-  const size_t need = mlp_ws(fmt, M, H, I, flags & 3);
+  const size_t need = mlp_ws(fmt, M, H, I, flags & (3 | WQ_ACT_E4M3));
   if (use_static) {
     if (need > WQ_STATIC_SCRATCH_BYTES) return WQ_ESCRATCH;
   } else if (ws == nullptr || ws_bytes < need) {
@@ -288,6 +323,26 @@ int mlp_run(int fmt, int64_t M, int64_t H, int64_t I, const void* x, int x_dtype
     return rc;
   }
   uint8_t* base = reinterpret_cast<uint8_t*>(ws);
+  if (w8) {
+    // W4A8: x quantized per token once for gate and up; act (float32) quantized the same way for down
+    const W8Ws L = w8_ws(M, H, I);
+    uint8_t* xq = base + L.xq;
+    float* sx = reinterpret_cast<float*>(base + L.sx);
+    float* act32 = reinterpret_cast<float*>(base + L.act32);
+    uint8_t* aq = base + L.aq;
+    float* sa = reinterpret_cast<float*>(base + L.sa);
+    float* partials = L.total > L.partials ? reinterpret_cast<float*>(base + L.partials) : nullptr;
+    if (do_gu) {
+      rc = launched(wq::launch_quant_e4m3(m, h, x, xt, xq, sx, st));
+      if (rc == WQ_OK)
+        rc = launched(wq::launch_w4a8_gateup(m, h, i, xq, sx, wg, 1.0f / gg, wu, 1.0f / gu, act32, partials, st));
+    }
+    if (rc == WQ_OK && do_down) {
+      rc = launched(wq::launch_quant_e4m3(m, i, act32, wq::X_F32, aq, sa, st));
+      if (rc == WQ_OK) rc = launched(wq::launch_w4a8_linear(m, i, h, aq, sa, wd, 1.0f / gd, out, partials, st));
+    }
+    return rc;
+  }
   const MfmaWs L = mfma_ws(fmt, M, H, I);
   uint16_t* x16 = reinterpret_cast<uint16_t*>(base + L.x16);
   float* rs = reinterpret_cast<float*>(base + L.rs);
@@ -345,8 +400,9 @@ const char* wq_strerror(int rc) {
 int wq_last_hip_error(void) { return g_last_hip; }
 
 size_t mlp_workspace_bytes(int fmt, int64_t M, int64_t H, int64_t I, int flags) {
-  if ((fmt != WQ_FMT_FP8W && fmt != WQ_FMT_NVFP4) || (flags & ~15) || (flags & 3) == 3) return 0;
-  return mlp_ws(fmt, M, H, I, flags & 3);
+  if ((fmt != WQ_FMT_FP8W && fmt != WQ_FMT_NVFP4) || (flags & ~31) || (flags & 3) == 3) return 0;
+  if ((flags & WQ_ACT_E4M3) && (flags & 3) == WQ_PATH_GEMV) return 0;
+  return mlp_ws(fmt, M, H, I, flags & (3 | WQ_ACT_E4M3));
 }
 
 int mlp_fp8w_run(int64_t M, int64_t H, int64_t I, const void* x, int x_dtype, const uint8_t* w_gate,
@@ -471,8 +527,12 @@ int wq_read_probe(const void* src, size_t bytes, uint32_t* sink, int grid, void*
 }
 
 size_t qlinear_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K, int flags) {
-  if ((fmt != WQ_FMT_FP8W && fmt != WQ_FMT_NVFP4) || flags < WQ_PATH_AUTO || flags > WQ_PATH_MFMA) return 0;
+  if ((fmt != WQ_FMT_FP8W && fmt != WQ_FMT_NVFP4) || (flags & ~(3 | WQ_ACT_E4M3)) || (flags & 3) == 3) return 0;
   if (M <= 0 || N <= 0 || K <= 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim || !elems_ok(M, N, K)) return 0;
+  if (flags & WQ_ACT_E4M3) {
+    if (fmt != WQ_FMT_NVFP4 || (flags & 3) == WQ_PATH_GEMV || !w8_k_ok(K)) return 0;
+    return align256((size_t)M * K) + align256((size_t)M * 4) + align256(wq::w4a8_partial_bytes((int)M, (int)K, (int)N, false));
+  }
   if (linear_path(fmt, M, N, K, flags) == WQ_PATH_GEMV) return 0;
   return align256((size_t)M * K * 2) + align256((size_t)M * 4) +
          align256(wq::mfma_partial_bytes(fmt == WQ_FMT_NVFP4 ? 1 : 0, (int)M, (int)K, (int)N, false));
@@ -482,10 +542,12 @@ int qlinear_run(int fmt, int64_t M, int64_t N, int64_t K, const void* x, int x_d
                 const float* scale, float global_scale, void* workspace, size_t workspace_bytes, float* y, int flags,
                 void* stream) {
   if (fmt != WQ_FMT_FP8W && fmt != WQ_FMT_NVFP4) return WQ_EINVAL;
-  if (flags < WQ_PATH_AUTO || flags > WQ_PATH_MFMA) return WQ_EINVAL;
+  if ((flags & ~(3 | WQ_ACT_E4M3)) || (flags & 3) == 3) return WQ_EINVAL;
+  const bool w8 = (flags & WQ_ACT_E4M3) != 0;   // W4A8: NVFP4 only, MFMA path only, float32 or bf16 x
+  if (w8 && (fmt != WQ_FMT_NVFP4 || (flags & 3) == WQ_PATH_GEMV || x_dtype == WQ_F16)) return WQ_EINVAL;
   if (x_dtype != WQ_F32 && x_dtype != WQ_BF16 && x_dtype != WQ_F16) return WQ_EINVAL;
   // float16 x: the operand type of the NVFP4 MLP's GEMV down projection; NVFP4 on the GEMV path only
-  if (x_dtype == WQ_F16 && (fmt != WQ_FMT_NVFP4 || flags == WQ_PATH_MFMA)) return WQ_EINVAL;
+  if (x_dtype == WQ_F16 && (fmt != WQ_FMT_NVFP4 || (flags & 3) == WQ_PATH_MFMA)) return WQ_EINVAL;
   if (M < 0 || M > kMaxDim || N <= 0 || K <= 0 || N > kMaxDim || K > kMaxDim || !elems_ok(M, N, K)) return WQ_EINVAL;
   const int path = x_dtype == WQ_F16 ? WQ_PATH_GEMV : linear_path(fmt, M, N, K, flags);
   // K runs along the records (NVFP4), the 64-wide MFMA K steps and the 16-byte FP8 chunks; N (output
@@ -496,6 +558,7 @@ int qlinear_run(int fmt, int64_t M, int64_t N, int64_t K, const void* x, int x_d
     return WQ_EINVAL;
   }
   if (path == WQ_PATH_GEMV && !gemv_fits(fmt, K, x_dtype)) return WQ_EINVAL;
+  if (w8 && !w8_k_ok(K)) return WQ_EINVAL;
   if (w == nullptr) return WQ_EINVAL;
   if (fmt == WQ_FMT_FP8W && scale == nullptr) return WQ_EINVAL;
   if (fmt == WQ_FMT_NVFP4 && (!(global_scale > 0.f) || !std::isfinite(global_scale))) return WQ_EINVAL;
@@ -519,6 +582,16 @@ int qlinear_run(int fmt, int64_t M, int64_t N, int64_t K, const void* x, int x_d
     return launched(wq::launch_nvfp4_gemv((int)M, (int)K, (int)N, x, xt, w, inv, nullptr, 0.f, y, false, st));
   }
   uint8_t* base = reinterpret_cast<uint8_t*>(workspace);
+  if (w8) {   // workspace: xq [M,K] E4M3 codes, sx [M], partials
+    uint8_t* xq = base;
+    float* sx = reinterpret_cast<float*>(base + align256((size_t)M * K));
+    float* partials = wq::w4a8_partial_bytes((int)M, (int)K, (int)N, false)
+                          ? reinterpret_cast<float*>(base + align256((size_t)M * K) + align256((size_t)M * 4))
+                          : nullptr;
+    rc = launched(wq::launch_quant_e4m3((int)M, (int)K, x, xt, xq, sx, st));
+    if (rc == WQ_OK) rc = launched(wq::launch_w4a8_linear((int)M, (int)K, (int)N, xq, sx, w, inv, y, partials, st));
+    return rc;
+  }
   uint16_t* x16 = reinterpret_cast<uint16_t*>(base);
   float* rs = reinterpret_cast<float*>(base + align256((size_t)M * K * 2));
   const int f = fmt == WQ_FMT_NVFP4 ? 1 : 0;
