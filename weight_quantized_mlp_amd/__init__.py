@@ -32,7 +32,8 @@ _PATHS = {"auto": WQ_PATH_AUTO, "gemv": WQ_PATH_GEMV, "mfma": WQ_PATH_MFMA}
 _STAGES = {None: 0, "gateup": WQ_STAGE_GATEUP_ONLY, "down": WQ_STAGE_DOWN_ONLY}
 _ACTS = {None: 0, "e4m3": WQ_ACT_E4M3}
 
-lib_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libwqmlp.so")
+# The in-tree library; WQMLP_LIBRARY names another build of it (the host-sanitizer build of the CPU tests).
+lib_path = os.environ.get("WQMLP_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libwqmlp.so")
 _lib = None
 
 _P = ctypes.c_void_p

@@ -27,30 +27,42 @@ def _hipcc():
     raise RuntimeError("hipcc not found")
 
 
-def _compile(src, obj, hipcc):
-    cmd = [hipcc, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj] + FLAGS
+# Host-only sanitizers (AddressSanitizer + UndefinedBehaviorSanitizer on the host code of every source; the
+# gfx950 code objects are built as usual).  Used by the CPU test that runs the ABI checks under them.
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def _compile(src, obj, hipcc, extra=()):
+    cmd = [hipcc, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj] + FLAGS + list(extra)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(verbose=False):
+def build(verbose=False, sanitize=False, out=None):
+    """Build the library.  sanitize=True adds the host-side sanitizers (SAN_FLAGS) and writes to `out`
+    (default _build/san/libwqmlp.so) instead of the in-tree library."""
     hipcc = _hipcc()
-    bdir = os.path.join(ROOT, "_build")
+    bdir = os.path.join(ROOT, "_build", "san" if sanitize else "")
     os.makedirs(bdir, exist_ok=True)
+    lib = (out or os.path.join(bdir, "libwqmlp.so")) if sanitize else LIB
+    extra = SAN_FLAGS if sanitize else ()
     objs = [os.path.join(bdir, os.path.splitext(s)[0] + ".o") for s in SOURCES]
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        list(ex.map(lambda a: _compile(a[0], a[1], hipcc), zip(SOURCES, objs)))
-    tmp = LIB + ".tmp"
+        list(ex.map(lambda a: _compile(a[0], a[1], hipcc, extra), zip(SOURCES, objs)))
+    tmp = lib + ".tmp"
     cmd = [hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
+    if sanitize:
+        cmd += ["-fsanitize=address,undefined", "-shared-libsan"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print("built", LIB)
-    return LIB
+        print("built", lib)
+    return lib
 
 
 if __name__ == "__main__":
