@@ -136,3 +136,32 @@ def test_rotating_ids_and_determinism(moe):
         ref_out, ref_act = oracle.moe_awq_m1_ref(d["x_bits"], ids, d["router_w"], d["w13"], d["w2"], I)
         gate(f64(out)[None], f64(ref_out)[None], what="moe rotating ids")
         check_act_bound(d, act, ref_act, ids)
+
+
+# Shapes reaching every kernel form of the step: W2 row-pair kernel with 1..4 groups per half row
+# (I = 32 .. 256), the piece kernel (I = 320, 512) and the per-row kernel (I = 1024); W13 with 1..8
+# groups per lane (H = 256 .. 4096) and its runtime loop (H = 8192); top-k 1, 3, 16.
+MOE_SHAPES = [(24, 3, 256, 32), (24, 16, 512, 64), (24, 1, 256, 96), (40, 10, 2048, 128), (24, 5, 768, 192),
+              (24, 4, 512, 256), (24, 3, 256, 320), (20, 2, 512, 512), (12, 2, 256, 1024), (12, 3, 8192, 64)]
+
+
+@pytest.mark.parametrize("E,topk,Hs,Is", MOE_SHAPES)
+@pytest.mark.parametrize("ml", [3, 4])
+def test_moe_shapes(E, topk, Hs, Is, ml):
+    d = synth.awq_moe(E=E, topk=topk, H=Hs, I=Is, config_id=50 + Is)
+    ids = d["ids"].copy()
+    if topk >= 3:
+        ids[1] = -1                                  # an invalid route
+        ids[2] = ids[0]                              # a duplicate
+    banks = tuple(dev(oracle.awq_pack_bank(*d[n], ml)) for n in ("w13", "w2"))
+    out, act = wq.moe_awq_m1_run(f16_dev(d["x_bits"]), dev(ids), dev(d["router_w"]), *banks, E, Is, ml)
+    out = host(out).view(np.uint16)
+    act = host(act).view(np.uint16)
+    ref_out, ref_act = oracle.moe_awq_m1_ref(d["x_bits"], ids, d["router_w"], d["w13"], d["w2"], Is)
+    valid = [r for r in range(topk) if 0 <= ids[r] < E]      # an invalid route's act row is all zeros
+    gate(f64(act)[valid], f64(ref_act)[valid], what=f"moe act E={E} k={topk} H={Hs} I={Is} layout {ml}")
+    gate(f64(out)[None], f64(ref_out)[None], what=f"moe out E={E} k={topk} H={Hs} I={Is} layout {ml}")
+    pair_out, _ = oracle.moe_w2_stage_ref(act, ids, d["router_w"], *d["w2"])
+    assert ulp_dist(out, pair_out).max() <= 4
+    if topk >= 3:
+        assert np.all(act[1] == 0) and np.array_equal(act[0], act[2])

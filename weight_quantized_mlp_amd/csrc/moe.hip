@@ -88,14 +88,35 @@ __device__ __forceinline__ _Float16 group_bias(const uint8_t* expert, const AwqL
   if constexpr (ML == 3) return awq_bias(expert[L.meta2_off + idx], s);
   else return f16_from_bits(reinterpret_cast<const uint16_t*>(expert + L.meta2_off)[idx]);
 }
+// The group's second metadata element as stored (zero byte or bias bits), and the bias made from it
+// later: loading the raw values first lets every load of a lane be issued before any of them is used
+// (a bias computed at load time makes the compiler wait for each group's metadata in turn).
+template <int ML>
+__device__ __forceinline__ uint32_t group_meta2_raw(const uint8_t* expert, const AwqLayout& L, int64_t idx) {
+  if constexpr (ML == 3) return expert[L.meta2_off + idx];
+  else return reinterpret_cast<const uint16_t*>(expert + L.meta2_off)[idx];
+}
+template <int ML>
+__device__ __forceinline__ _Float16 group_bias_from_raw(uint32_t raw, _Float16 s) {
+  if constexpr (ML == 3) return awq_bias(raw, s);
+  else return f16_from_bits((uint16_t)raw);
+}
 
 // GPL: groups per lane (compile-time, so every weight load of a lane is issued at once before the
 // activations are staged); 0 = runtime loop for shapes outside the unrolled range.
+// W2 prefetch: while its own weight loads are in flight, each W13 workgroup also reads its share (one
+// gridDim.y-th) of its route's W2 expert block, so that the W2 kernel finds those bytes in the
+// memory-side cache instead of waiting a DRAM round trip.  The values only feed an empty asm at the end
+// (kept live, never stored).  kPrefetchPerThread 16-byte loads per thread cover a 20-workgroup route of a
+// 243 KB W2 expert (3-byte metadata) and most of a 4-byte one.
+constexpr int kPrefetchPerThread = 3;   // (the end-of-kernel asm below names three)
+
 template <int ML, int GPL>
 __global__ void __launch_bounds__(256) awq_w13_kernel(int E, int H, int I, const uint16_t* __restrict__ x,
                                                       const int32_t* __restrict__ ids,
                                                       const uint8_t* __restrict__ bank, AwqLayout L,
-                                                      uint16_t* __restrict__ act) {
+                                                      uint16_t* __restrict__ act,
+                                                      const uint8_t* __restrict__ w2bank, int64_t w2_expert_bytes) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int r = blockIdx.x;
   const int nb = blockIdx.y * 8;
@@ -115,28 +136,38 @@ __global__ void __launch_bounds__(256) awq_w13_kernel(int E, int H, int I, const
   const uint8_t* codes = expert + (size_t)row * (H >> 1);
   const uint16_t* scales = reinterpret_cast<const uint16_t*>(expert + L.scale_off);
   float acc = 0.f;
+  u32x4 pf[kPrefetchPerThread];
+  // this workgroup's share of the route's W2 expert block, 16-byte units [u0, u1)
+  const int64_t w2_units = w2_expert_bytes >> 4;
+  const int64_t per_wg = (w2_units + gridDim.y - 1) / gridDim.y;
+  const int64_t u0 = (int64_t)blockIdx.y * per_wg;
+  const u32x4* w2e = reinterpret_cast<const u32x4*>(w2bank + (size_t)e * w2_expert_bytes);
   if constexpr (GPL > 0) {
+    // Every load is unconditional, from a clamped in-bounds address (groups past G read group G-1 and are
+    // not used): a load under a condition leaves a join at which the compiler copies the loaded register,
+    // and the copy waits for the load, which serialises the memory round trips.  (I is a multiple of 8, so
+    // every row n of the workgroup exists.)
     u32x4 c[GPL];
-    _Float16 sv[GPL], bv[GPL];
-    if (n < I) {
+    uint32_t sraw[GPL], mraw[GPL];
 #pragma unroll
-      for (int i = 0; i < GPL; ++i) {
-        const int g = j + 16 * i;
-        if (g < G) {
-          const int64_t mi = (int64_t)row * G + g;
-          c[i] = *reinterpret_cast<const u32x4*>(codes + 16 * g);
-          sv[i] = f16_from_bits(scales[mi]);
-          bv[i] = group_bias<ML>(expert, L, mi, sv[i]);
-        }
-      }
+    for (int i = 0; i < GPL; ++i) {
+      const int g = min(j + 16 * i, G - 1);
+      const int64_t mi = (int64_t)row * G + g;
+      c[i] = *reinterpret_cast<const u32x4*>(codes + 16 * g);
+      sraw[i] = scales[mi];
+      mraw[i] = group_meta2_raw<ML>(expert, L, mi);
     }
+#pragma unroll
+    for (int i = 0; i < kPrefetchPerThread; ++i)
+      pf[i] = w2e[min(u0 + tid + 256 * i, (int64_t)w2_units - 1)];   // past the share: repeats a byte range
     stage_pairs(lds, x, H, 1, 0);
     __syncthreads();
-    if (n < I) {
 #pragma unroll
-      for (int i = 0; i < GPL; ++i) {
-        const int g = j + 16 * i;
-        if (g < G) acc = awq_group_dot(c[i], sv[i], bv[i], lds + g * kGrpStride, acc);
+    for (int i = 0; i < GPL; ++i) {
+      if (j + 16 * i < G) {
+        const _Float16 sv = f16_from_bits((uint16_t)sraw[i]);
+        acc = awq_group_dot(c[i], sv, group_bias_from_raw<ML>(mraw[i], sv), lds + j * kGrpStride + 16 * i * kGrpStride,
+                            acc);
       }
     }
   } else {
@@ -160,6 +191,8 @@ __global__ void __launch_bounds__(256) awq_w13_kernel(int E, int H, int I, const
     const _Float16 a = (_Float16)(silu_f32(gh) * uh);
     act[(size_t)r * I + n] = __builtin_bit_cast(uint16_t, a);
   }
+  if constexpr (GPL > 0)   // the prefetched W2 bytes, consumed by nothing (only the wait at the very end)
+    asm volatile("" ::"v"(pf[0]), "v"(pf[1]), "v"(pf[2]));
 }
 
 // Kernel 2 (W2 + ordered sum): one workgroup per kW2Rows outputs, one wave per route.  Wave r reads the
@@ -194,15 +227,15 @@ __global__ void __launch_bounds__(1024) awq_w2_kernel(int E, int topk, int H, in
   const uint16_t* scales = reinterpret_cast<const uint16_t*>(expert + L.scale_off);
   const int64_t m0 = (int64_t)o0 * G;
   u32x4 c[PPL];
-  _Float16 sv[PPL], bv[PPL];
+  uint32_t sraw[PPL], mraw[PPL];
   if (live) {
 #pragma unroll
     for (int j = 0; j < PPL; ++j) {
       const int pc = lane + 64 * j;
       if (pc < np) {
         c[j] = *reinterpret_cast<const u32x4*>(codes + 16 * pc);
-        sv[j] = f16_from_bits(scales[m0 + pc]);
-        bv[j] = group_bias<ML>(expert, L, m0 + pc, sv[j]);
+        sraw[j] = scales[m0 + pc];
+        mraw[j] = group_meta2_raw<ML>(expert, L, m0 + pc);
       }
     }
   }
@@ -213,8 +246,10 @@ __global__ void __launch_bounds__(1024) awq_w2_kernel(int E, int topk, int H, in
     const int pc = lane + 64 * j;
     if (pc < np) {
       const int g = pc % G;
+      const _Float16 sv = f16_from_bits((uint16_t)sraw[j]);
       part[(r * kW2Rows) * G + pc] =
-          live ? awq_group_dot(c[j], sv[j], bv[j], lds + r * act_bytes + g * kGrpStride, 0.f) : 0.f;
+          live ? awq_group_dot(c[j], sv, group_bias_from_raw<ML>(mraw[j], sv), lds + r * act_bytes + g * kGrpStride, 0.f)
+               : 0.f;
     }
   }
   __syncthreads();
@@ -233,6 +268,87 @@ __global__ void __launch_bounds__(1024) awq_w2_kernel(int E, int topk, int H, in
       if (er >= 0 && er < E) sum = fmaf(router_w[rr], ys[rr * kW2Rows + tid], sum);
     }
     out[o0 + tid] = __builtin_bit_cast(uint16_t, (_Float16)sum);
+  }
+}
+
+// Kernel 2, row-pair form (G = I/32 <= 8): one workgroup per 32 outputs, one wave per route; lane l handles
+// row o0 + (l & 31) and half h = l >> 5 of its groups (h = 0: groups [0, GH), h = 1: [GH, G), GH = ceil(G/2)).
+// The lane loads its groups' codes and metadata and its route's act for those groups straight into
+// registers (act is read by all 32 lanes of a half at the same addresses), so nothing is staged in LDS
+// before the dot products.  Order per (route, row): each group's 16 dot2 steps from 0, the group partials
+// of a half added in group order, then half 0 + half 1, rounded to float16; one barrier, then 32 threads
+// add the routes in order with fmaf.
+constexpr int kMaxRoutes = 16;   // the entry point's top-k limit (one wave per route, 1024 threads)
+
+template <int ML, int GH>
+__global__ void __launch_bounds__(1024) awq_w2_pair_kernel(int E, int topk, int H, int I,
+                                                           const int32_t* __restrict__ ids,
+                                                           const float* __restrict__ router_w,
+                                                           const uint8_t* __restrict__ bank, AwqLayout L,
+                                                           const uint16_t* __restrict__ act, uint16_t* __restrict__ out) {
+  __shared__ float ys[kMaxRoutes][32];
+  const int G = I >> 5;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int r = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int row = lane & 31, h = lane >> 5;
+  const int o = blockIdx.x * 32 + row;
+  const int g0 = h * GH;
+  const int ng = h ? G - GH : GH;                     // this half's group count (0 < ng <= GH)
+  const int e = ids[r];
+  const bool live = e >= 0 && e < E;
+  const uint8_t* expert = bank + (size_t)(live ? e : 0) * L.expert_bytes;
+  const uint8_t* codes = expert + (size_t)o * (I >> 1);
+  const uint16_t* scales = reinterpret_cast<const uint16_t*>(expert + L.scale_off);
+  const u32x4* ar = reinterpret_cast<const u32x4*>(act + (size_t)r * I);   // 8 halves per 16-byte chunk
+  // unconditional loads from clamped addresses (an invalid id reads expert 0; groups past this half's
+  // count read group G-1), so that every load of the lane is in flight before any is used
+  u32x4 c[GH], a[GH][4];
+  uint32_t sraw[GH], mraw[GH];
+#pragma unroll
+  for (int i = 0; i < GH; ++i) {
+    const int g = min(g0 + i, G - 1);
+    const int64_t mi = (int64_t)o * G + g;
+    c[i] = *reinterpret_cast<const u32x4*>(codes + 16 * g);
+    sraw[i] = scales[mi];
+    mraw[i] = group_meta2_raw<ML>(expert, L, mi);
+  }
+#pragma unroll
+  for (int i = 0; i < GH; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) a[i][q] = ar[4 * min(g0 + i, G - 1) + q];
+  // every group's partial is computed (a group past this half's count from its clamped copy) and only the
+  // valid ones are added, in group order: with the uses unconditional the loads above stay where they are
+  // (a conditional use lets the compiler sink its loads into the condition, one round trip each)
+  float acc = 0.f;
+#pragma unroll
+  for (int i = 0; i < GH; ++i) {
+    const _Float16 sv = f16_from_bits((uint16_t)sraw[i]), bv = group_bias_from_raw<ML>(mraw[i], sv);
+    const f16x2 s2 = {sv, sv}, b2 = {bv, bv};
+    float p = 0.f;
+#pragma unroll
+    for (int dw = 0; dw < 4; ++dw) {
+      const u32x4 v = a[i][dw];               // k = 8 dw .. 8 dw + 7 of the group, natural order
+      const uint32_t x04 = (v.x & 0xffffu) | (v.z << 16), x15 = (v.x >> 16) | (v.z & 0xffff0000u);
+      const uint32_t x26 = (v.y & 0xffffu) | (v.w << 16), x37 = (v.y >> 16) | (v.w & 0xffff0000u);
+      const uint32_t w = c[i][dw];
+      p = dot2_f16(awq_pair<0>(w, s2, b2), as_f16x2(x04), p);
+      p = dot2_f16(awq_pair<1>(w, s2, b2), as_f16x2(x15), p);
+      p = dot2_f16(awq_pair<2>(w, s2, b2), as_f16x2(x26), p);
+      p = dot2_f16(awq_pair<3>(w, s2, b2), as_f16x2(x37), p);
+    }
+    acc = i < ng ? acc + p : acc;
+  }
+  const float other = __shfl_xor(acc, 32, 64);      // the row's other half
+  if (h == 0 && r < topk) ys[r][row] = live ? (float)(_Float16)(acc + other) : 0.f;   // per-route float16
+  __syncthreads();
+  if (tid < 32) {
+    float sum = 0.f;
+    for (int rr = 0; rr < topk; ++rr) {
+      const int er = ids[rr];
+      if (er >= 0 && er < E) sum = fmaf(router_w[rr], ys[rr][tid], sum);
+    }
+    out[blockIdx.x * 32 + tid] = __builtin_bit_cast(uint16_t, (_Float16)sum);
   }
 }
 
@@ -295,7 +411,8 @@ hipError_t launch_moe_awq_m1(int E, int topk, int H, int I, const uint16_t* x, c
   const dim3 g13(topk, (I + 7) / 8);
   const int gpl13 = (H / 32 + 15) / 16;  // groups per lane in W13
 #define WQ_W13(ML, P)                                                                                     \
-  hipLaunchKernelGGL((awq_w13_kernel<ML, P>), g13, dim3(256), lds13, st, E, H, I, x, ids, w13, L13, act)
+  hipLaunchKernelGGL((awq_w13_kernel<ML, P>), g13, dim3(256), lds13, st, E, H, I, x, ids, w13, L13, act, w2, \
+                     L2.expert_bytes)
 #define WQ_W13_ML(ML)                                                                     \
   switch (gpl13) {                                                                        \
     case 1: WQ_W13(ML, 1); break;                                                         \
@@ -319,7 +436,27 @@ hipError_t launch_moe_awq_m1(int E, int topk, int H, int I, const uint16_t* x, c
   if (err != hipSuccess) return err;
   const size_t lds2 = (size_t)topk * (I / 32) * kGrpStride + (size_t)topk * kW2Rows * (I / 32 + 1) * 4;
   const int ppl2 = (kW2Rows * (I / 32) + 63) / 64;  // 16-byte pieces per lane in W2
-  if (ppl2 <= 8 && lds2 <= 65536) {
+  const int gh = (I / 32 + 1) / 2;                  // groups per half row in the row-pair form
+  if (gh <= 4) {
+    const dim3 g2(H / 32);
+#define WQ_W2P(ML, GH)                                                                                           \
+  hipLaunchKernelGGL((awq_w2_pair_kernel<ML, GH>), g2, dim3(64 * topk), 0, st, E, topk, H, I, ids, router_w, w2, L2, \
+                     act, out)
+#define WQ_W2P_ML(ML)              \
+  switch (gh) {                    \
+    case 1: WQ_W2P(ML, 1); break;  \
+    case 2: WQ_W2P(ML, 2); break;  \
+    case 3: WQ_W2P(ML, 3); break;  \
+    default: WQ_W2P(ML, 4); break; \
+  }
+    if (meta_layout == 3) {
+      WQ_W2P_ML(3)
+    } else {
+      WQ_W2P_ML(4)
+    }
+#undef WQ_W2P_ML
+#undef WQ_W2P
+  } else if (ppl2 <= 8 && lds2 <= 65536) {
     const dim3 g2((H + kW2Rows - 1) / kW2Rows);
 #define WQ_W2(ML, P)                                                                                          \
   hipLaunchKernelGGL((awq_w2_kernel<ML, P>), g2, dim3(64 * topk), lds2, st, E, topk, H, I, ids, router_w, w2, L2, \
