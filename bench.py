@@ -71,6 +71,8 @@ def parse():
                     help="only run this many plain FP8 M=512 prefill steps (bf16 x, 2 weight copies), for rocprofv3")
     ap.add_argument("--awq-counters", type=int, default=0,
                     help="only run this many plain routed-expert steps over rotating experts, for rocprofv3")
+    ap.add_argument("--w4a8-counters", type=int, default=0,
+                    help="run N plain W4A8 prefill steps (M=512) and exit (for rocprofv3)")
     ap.add_argument("--json-out", default=None)
     a = ap.parse_args()
     a.samples = max(7, a.samples)
@@ -557,6 +559,22 @@ def counter_modes(args, torch, wq, synth, dev):
             step(i)
         torch.cuda.synchronize()
         log(f"fp8 prefill counter steps done: {args.fp8_prefill_counters}")
+        return True
+    if args.w4a8_counters:
+        blk, gs = nvfp4_weights(torch, wq, synth.nvfp4_mlp_weights(), dev)
+        M = 512
+        sets = [blk, {k: t.clone() for k, t in blk.items()}]
+        xb, _ = synth.nvfp4_x(M, outlier_frac=0.01)
+        x = torch.from_numpy(xb.view("int16")).to(dev).view(torch.bfloat16)
+        out = torch.empty((M, H), dtype=torch.float32, device=dev)
+        ws = torch.empty(wq.mlp_workspace_bytes(wq.WQ_FMT_NVFP4, M, H, I, "auto", "e4m3"), dtype=torch.uint8,
+                         device=dev)
+        for i in range(args.w4a8_counters):
+            b = sets[i % 2]
+            wq.mlp_nvfp4_run(x, b["gate"], gs["gate"], b["up"], gs["up"], b["down"], gs["down"], out=out,
+                             workspace=ws, act="e4m3")
+        torch.cuda.synchronize()
+        log(f"w4a8 prefill counter steps done: {args.w4a8_counters}")
         return True
     if args.awq_counters:
         a = awq_run(torch, wq, synth, synth.awq_moe(), 7, calls=args.awq_counters)
