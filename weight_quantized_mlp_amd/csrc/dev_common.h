@@ -83,6 +83,37 @@ __device__ __forceinline__ void lds_copy16(uint32_t voff, const void* sbase, uin
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds_base)
                : "memory", "m0");
 }
+// A run of N <= 4 such copies with one M0 write: copy k reads b[k] + v[k] + 1024 k into LDS at
+// lds_base + 1024 k + 16 * lane.  The instruction's offset field adds 1024 k to both the global and the LDS
+// address, so callers pass each global base lowered by 1024 k (only the sum is an address).  Rewriting M0
+// before every copy cost 3% of the prefill GEMM's time.
+template <int N>
+__device__ __forceinline__ void lds_copy16_run(const uint32_t* v, const uint8_t* const* b, uint32_t lds_base) {
+  static_assert(N >= 1 && N <= 4, "run length");
+  if constexpr (N == 1) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(v[0]), "s"(b[0]),
+                 "s"(lds_base)
+                 : "memory", "m0");
+  } else if constexpr (N == 2) {
+    asm volatile(
+        "s_mov_b32 m0, %4\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %2\n\tglobal_load_lds_dwordx4 %1, %3 offset:1024" ::"v"(
+            v[0]),
+        "v"(v[1]), "s"(b[0]), "s"(b[1]), "s"(lds_base)
+        : "memory", "m0");
+  } else if constexpr (N == 3) {
+    asm volatile(
+        "s_mov_b32 m0, %6\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %3\n\tglobal_load_lds_dwordx4 %1, %4 offset:1024\n\t"
+        "global_load_lds_dwordx4 %2, %5 offset:2048" ::"v"(v[0]),
+        "v"(v[1]), "v"(v[2]), "s"(b[0]), "s"(b[1]), "s"(b[2]), "s"(lds_base)
+        : "memory", "m0");
+  } else {
+    asm volatile(
+        "s_mov_b32 m0, %8\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %4\n\tglobal_load_lds_dwordx4 %1, %5 offset:1024\n\t"
+        "global_load_lds_dwordx4 %2, %6 offset:2048\n\tglobal_load_lds_dwordx4 %3, %7 offset:3072" ::"v"(v[0]),
+        "v"(v[1]), "v"(v[2]), "v"(v[3]), "s"(b[0]), "s"(b[1]), "s"(b[2]), "s"(b[3]), "s"(lds_base)
+        : "memory", "m0");
+  }
+}
 #pragma clang diagnostic pop
 // s_waitcnt vmcnt(N) with the other counters left alone (the copies above are invisible to the compiler's
 // own counter tracking, so every wait on them is explicit).

@@ -556,13 +556,15 @@ __global__ void __launch_bounds__(256, 2) nv_gemm_kernel(int M, int K, int N, Nv
   const uint32_t wlds = lds0 + AS * kNvAStage + wave * g_wave_wbytes<FMT>(GU);
   const uint8_t* wbuf = lds + AS * kNvAStage + wave * g_wave_wbytes<FMT>(GU);
 
-  // Activation chunk p = tid + 256 i: tile row p >> 3, LDS chunk p & 7, global chunk (p & 7) ^ (row & 7).
-  // Offsets are relative to the tile's first row (64-bit base), so they stay below 32 * MB * K * 2 bytes.
+  // Activation chunk p = 64 MB wave + 64 i + lane (copy i of the wave): tile row p >> 3, LDS chunk p & 7,
+  // global chunk (p & 7) ^ (row & 7).  A wave's MB copies are consecutive kilobytes of the stage, so they go
+  // out as one run with one M0 write.  Offsets are relative to the tile's first row (64-bit base), so they
+  // stay below 32 * MB * K * 2 bytes.
   const uint8_t* a_tile = reinterpret_cast<const uint8_t*>(a16) + (size_t)m0 * K * 2;
   uint32_t aoff[MB];
 #pragma unroll
   for (int i = 0; i < MB; ++i) {
-    const int p = tid + 256 * i, row = p >> 3, c = p & 7;
+    const int p = 64 * MB * wave + 64 * i + lane, row = p >> 3, c = p & 7;
     aoff[i] = (uint32_t)(min(m0 + row, M - 1) - m0) * (uint32_t)K * 2u + (uint32_t)((c ^ (row & 7)) * 16);
   }
   // Weight copy j = CPM t + i of matrix t writes LDS slot s = 64 i + lane of the matrix's block buffer
@@ -589,18 +591,18 @@ __global__ void __launch_bounds__(256, 2) nv_gemm_kernel(int M, int K, int N, Nv
     }
     woff[j] = (uint32_t)(min(n0 + 32 * wave + c, N - 1) - nw0) * rb + 16u * (uint32_t)q;
   }
-  // Copy i of a wave moves tile rows 8 wave + 32 i .. + 7.  Under the block schedule (which waits for all
-  // of a wave's copies at once) copies whose rows all lie past M are skipped: those rows' outputs are
-  // never stored, so their LDS rows may hold anything.  The stepped schedule counts copies in its waits
-  // and always issues them.
+  // Copy i of a wave moves tile rows 8 MB wave + 8 i .. + 7.  Under the block schedule (32-row tiles, one
+  // copy per wave, which waits for all of a wave's copies at once) a copy whose rows all lie past M is
+  // skipped: those rows' outputs are never stored, so their LDS rows may hold anything.  The stepped
+  // schedule counts copies in its waits and always issues them.
   auto copy_a = [&](int kt, int stage) {
     kt = min(kt, nk - 1);
     const uint8_t* base = a_tile + (size_t)kt * 128;
-    const uint32_t sb = lds0 + stage * kNvAStage;
+    const uint32_t sb = __builtin_amdgcn_readfirstlane(lds0 + stage * kNvAStage + 1024 * MB * wave);
+    const uint8_t* bases[MB];
 #pragma unroll
-    for (int i = 0; i < MB; ++i)
-      if (!BS || m0 + 8 * wave + 32 * i < M)
-        lds_copy16(aoff[i], base, __builtin_amdgcn_readfirstlane(sb + (256 * i + 64 * wave) * 16));
+    for (int i = 0; i < MB; ++i) bases[i] = base - 1024 * i;
+    if (!BS || m0 + 8 * MB * wave < M) lds_copy16_run<MB>(aoff, bases, sb);
   };
   // A row whose K-step count r = nk % KSB is not 0 ends in a short block: it is copied as the last CB
   // bytes of the row (steps KSB - r .. KSB - 1 of the window are the valid ones; K >= g_min_k, so the
@@ -609,9 +611,20 @@ __global__ void __launch_bounds__(256, 2) nv_gemm_kernel(int M, int K, int N, Nv
   auto copy_w = [&](int blk) {
     blk = min(blk, nblk - 1);
     const uint32_t boff = (rtail && blk == nblk - 1) ? rb - (uint32_t)CB : (uint32_t)blk * CB;
+    // runs of up to four copies, each run with one M0 write (copy j lands at wlds + 1024 j)
+    uint32_t v[NW];
+    const uint8_t* bases[NW];
 #pragma unroll
-    for (int j = 0; j < NW; ++j)
-      lds_copy16(woff[j] + boff, j < CPM ? wbase0 : wbase1, __builtin_amdgcn_readfirstlane(wlds + 1024 * j));
+    for (int j = 0; j < NW; ++j) {
+      v[j] = woff[j] + boff;
+      bases[j] = (j < CPM ? wbase0 : wbase1) - 1024 * (j & 3);
+    }
+#pragma unroll
+    for (int g = 0; g < NW; g += 4) {
+      const uint32_t lb = __builtin_amdgcn_readfirstlane(wlds + 1024 * g);
+      if (g + 4 <= NW) lds_copy16_run<4>(v + g, bases + g, lb);
+      else lds_copy16_run<(NW % 4 == 0 ? 4 : NW % 4)>(v + g, bases + g, lb);
+    }
   };
 
   f32x16 acc[NM][MB];
@@ -1238,9 +1251,20 @@ __global__ void __launch_bounds__(256, 2) w4a8_gemm_kernel(int M, int K, int N, 
   auto copy_w = [&](int blk) {
     blk = min(blk, nblk - 1);
     const uint32_t boff = (rtail && blk == nblk - 1) ? rb - (uint32_t)CB : (uint32_t)blk * CB;
+    // runs of up to four copies, each run with one M0 write (copy j lands at wlds + 1024 j)
+    uint32_t v[NW];
+    const uint8_t* bases[NW];
 #pragma unroll
-    for (int j = 0; j < NW; ++j)
-      lds_copy16(woff[j] + boff, j < CPM ? wbase0 : wbase1, __builtin_amdgcn_readfirstlane(wlds + 1024 * j));
+    for (int j = 0; j < NW; ++j) {
+      v[j] = woff[j] + boff;
+      bases[j] = (j < CPM ? wbase0 : wbase1) - 1024 * (j & 3);
+    }
+#pragma unroll
+    for (int g = 0; g < NW; g += 4) {
+      const uint32_t lb = __builtin_amdgcn_readfirstlane(wlds + 1024 * g);
+      if (g + 4 <= NW) lds_copy16_run<4>(v + g, bases + g, lb);
+      else lds_copy16_run<(NW % 4 == 0 ? 4 : NW % 4)>(v + g, bases + g, lb);
+    }
   };
 
   f32x16 acc[NM][MB];
