@@ -31,8 +31,9 @@
 // column load of weight bytes touches one cache line per lane, and that access pattern, not bandwidth,
 // limited the register-load form (mfma_gemm_kernel, kept for shorter K).  Here both operands move by
 // direct global->LDS copies (global_load_lds_dwordx4) in a coalesced order: the activation tile
-// (128-byte rows, 16-byte chunk c of row r stored at chunk c ^ (r & 7), so fragment reads are
-// bank-conflict free) in a 2-stage ring, and the weights in blocks per column (NVFP4: 4 records = 144
+// (128-byte rows, 16-byte chunk c of row r stored at chunk c ^ ((r >> 1) & 7): with 64 four-byte banks,
+// rows two apart share banks, and this swizzle gives the 8 rows of each parity among 16 consecutive lanes
+// 8 distinct chunks; c ^ (r & 7) gives them 4, and measured the same within 0.4%) in a 2-stage ring, and the weights in blocks per column (NVFP4: 4 records = 144
 // contiguous bytes; FP8: 2 K steps = 128 code bytes, chunk-swizzled), one block buffer per wave.  At
 // the start of a block each wave reads the whole block of its columns into registers and immediately
 // refills the buffer with the next block, so the weight copy has the block's K steps to land.  Inside
@@ -557,7 +558,7 @@ __global__ void __launch_bounds__(256, 2) nv_gemm_kernel(int M, int K, int N, Nv
   const uint8_t* wbuf = lds + AS * kNvAStage + wave * g_wave_wbytes<FMT>(GU);
 
   // Activation chunk p = 64 MB wave + 64 i + lane (copy i of the wave): tile row p >> 3, LDS chunk p & 7,
-  // global chunk (p & 7) ^ (row & 7).  A wave's MB copies are consecutive kilobytes of the stage, so they go
+  // global chunk (p & 7) ^ ((row >> 1) & 7).  A wave's MB copies are consecutive kilobytes of the stage, so they go
   // out as one run with one M0 write.  Offsets are relative to the tile's first row (64-bit base), so they
   // stay below 32 * MB * K * 2 bytes.
   const uint8_t* a_tile = reinterpret_cast<const uint8_t*>(a16) + (size_t)m0 * K * 2;
@@ -565,7 +566,7 @@ __global__ void __launch_bounds__(256, 2) nv_gemm_kernel(int M, int K, int N, Nv
 #pragma unroll
   for (int i = 0; i < MB; ++i) {
     const int p = 64 * MB * wave + 64 * i + lane, row = p >> 3, c = p & 7;
-    aoff[i] = (uint32_t)(min(m0 + row, M - 1) - m0) * (uint32_t)K * 2u + (uint32_t)((c ^ (row & 7)) * 16);
+    aoff[i] = (uint32_t)(min(m0 + row, M - 1) - m0) * (uint32_t)K * 2u + (uint32_t)((c ^ ((row >> 1) & 7)) * 16);
   }
   // Weight copy j = CPM t + i of matrix t writes LDS slot s = 64 i + lane of the matrix's block buffer
   // (wbuf + MBYTES t).  NVFP4: column c = s / 9, chunk q = s % 9 of the column's 144-byte block (slots
@@ -699,7 +700,7 @@ __global__ void __launch_bounds__(256, 2) nv_gemm_kernel(int M, int K, int N, Nv
     const uint8_t* ast = lds + stage * kNvAStage;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
-      af[mb] = *reinterpret_cast<const AFrag*>(ast + (32 * mb + li) * 128 + (((4 * h + s) ^ (li & 7)) * 16));
+      af[mb] = *reinterpret_cast<const AFrag*>(ast + (32 * mb + li) * 128 + (((4 * h + s) ^ ((li >> 1) & 7)) * 16));
   };
   // decode sub-step s of step J into exact f16 (NVFP4: E2M1 x E4M3 group scale; FP8: the E4M3 codes)
   // and run its MFMAs
@@ -1220,13 +1221,13 @@ __global__ void __launch_bounds__(256, 2) w4a8_gemm_kernel(int M, int K, int N, 
   const uint32_t wlds = lds0 + 2 * kAStage + wave * NM * MBYTES;
   const uint8_t* wbuf = lds + 2 * kAStage + wave * NM * MBYTES;
 
-  // activation codes: tile row p >> 3, LDS chunk p & 7 holds global chunk (p & 7) ^ (row & 7) of the step
+  // activation codes: tile row p >> 3, LDS chunk p & 7 holds global chunk (p & 7) ^ ((row >> 1) & 7) of the step
   const uint8_t* a_tile = aq + (size_t)m0 * K;
   uint32_t aoff[MB];
 #pragma unroll
   for (int i = 0; i < MB; ++i) {
     const int p = tid + 256 * i, row = p >> 3, c = p & 7;
-    aoff[i] = (uint32_t)(min(m0 + row, M - 1) - m0) * (uint32_t)K + (uint32_t)((c ^ (row & 7)) * 16);
+    aoff[i] = (uint32_t)(min(m0 + row, M - 1) - m0) * (uint32_t)K + (uint32_t)((c ^ ((row >> 1) & 7)) * 16);
   }
   const int nw0 = min(n0 + 32 * wave, N - 1);
   const uint8_t* wbase0 = w0 + (size_t)nw0 * rb;
@@ -1305,7 +1306,7 @@ __global__ void __launch_bounds__(256, 2) w4a8_gemm_kernel(int M, int K, int N, 
     const uint8_t* ast = lds + stage * kAStage;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
-      af[mb] = *reinterpret_cast<const long*>(ast + (32 * mb + li) * 128 + ((s ^ (li & 7)) * 16) + 8 * h);
+      af[mb] = *reinterpret_cast<const long*>(ast + (32 * mb + li) * 128 + ((s ^ ((li >> 1) & 7)) * 16) + 8 * h);
   };
   // group S (0..7) of step J of the block in registers: one K = 16 MFMA per (row block, matrix) into a
   // fresh partial, each partial scaled by its group scale and added while the next MFMA runs
