@@ -72,13 +72,14 @@ enum { WQ_STAGE_GATEUP_ONLY = 4, WQ_STAGE_DOWN_ONLY = 8 };
  * WQ_ACT_E4M3 selects the W4A8 variant (page "Qwen3.8-27B-NVFP4", section "Implemented execution
  * path": per-token dynamic 8-bit activations in a small workspace, one quantization of x shared by
  * gate and up).  Each row of the linear's input is scaled by the power of two 2^-e that puts its
- * largest magnitude in (224, 448] (exact) and encoded to E4M3 with round to nearest even; the NVFP4
- * weights decode exactly to E4M3 and every 16-wide E4M3 weight group runs as one K = 16 E4M3 MFMA
- * whose float32 result is scaled by the group's E4M3 scale.  The MLP quantizes x for gate/up and its
- * float32 act for down.  The activation rounding is the variant's own error against the exact MLP (the
- * page reports 1.458e-2 for its INT8 form; section "Correctness and precision").  Both dimensions that
- * act as K (H and I for the MLP, K for the linear) must be multiples of 128 and at least 256; with
- * WQ_PATH_GEMV, with FP8 weights or with float16 x the call is WQ_EINVAL. */
+ * largest magnitude in (224, 448] (exact) and rounded to E4M3 with round to nearest even.  Every E4M3
+ * value is a float16, as is every decoded NVFP4 weight (E2M1 x E4M3 group scale), so the quantized rows
+ * are held as float16 and the float16 MFMA GEMM forms each product exactly, accumulating in float32;
+ * out = (1/gs) 2^e sum_k e2m1 * d_group * xq.  The MLP quantizes x for gate/up and its float32 act for
+ * down.  The activation rounding is the variant's own error against the exact MLP (the page reports
+ * 1.458e-2 for its INT8 form; section "Correctness and precision").  Both dimensions that act as K (H
+ * and I for the MLP, K for the linear) must be multiples of 64 and at least 256; with WQ_PATH_GEMV,
+ * with FP8 weights or with float16 x the call is WQ_EINVAL. */
 enum { WQ_ACT_E4M3 = 16 };
 #define WQ_MFMA_MIN_ROWS 128
 #define WQ_NARROW_MIN_ROWS_NVFP4 3
@@ -113,9 +114,10 @@ int wq_last_hip_error(void);
  *              then float32 split-K partial tiles of at most 64 MiB; each
  *              region 256-byte aligned.  The size is a function of the shape
  *              alone.
- *   WQ_ACT_E4M3 (NVFP4): x codes uint8 [M, H], their row scales float32 [M],
- *              act float32 [M, I], act codes uint8 [M, I], their row scales
- *              float32 [M], then the split-K partial tiles; each region
+ *   WQ_ACT_E4M3 (NVFP4): x's E4M3 values as float16 [M, H] (each row times the
+ *              inverse of its scale), their row scales float32 [M], act
+ *              float32 [M, I], act's E4M3 values as float16 [M, I], their row
+ *              scales float32 [M], then the split-K partial tiles; each region
  *              256-byte aligned.  0 with WQ_PATH_GEMV or FP8.
  */
 size_t mlp_workspace_bytes(int fmt, int64_t M, int64_t H, int64_t I, int flags);
@@ -310,7 +312,7 @@ int awq_dequant_f16(int64_t E, int64_t N, int64_t K, const void* bank, int meta_
  *   none; the query does not know x's type and may ask for more than a float16
  *   call uses).
  * flags: a WQ_PATH_* value, plus WQ_ACT_E4M3 for NVFP4 (x quantized per row to
- * E4M3 as described there; MFMA path; K a multiple of 128, at least 256).
+ * E4M3 as described there; MFMA path; K a multiple of 64, at least 256).
  * Shapes: K a positive multiple of 64 for NVFP4 and for the MFMA path, else of
  * 16; N any positive row count (partial tiles are masked, as in the tail case of
  * page "Qwen3.8-27B-NVFP4", section "Correctness and precision": 129 x 67 x 320).

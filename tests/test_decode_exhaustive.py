@@ -140,8 +140,8 @@ H, I = 512, 384          # gate/up [I, H]: rows 0..255 exhaustive, 256..383 rand
 
 def act_view(ws, fmt, path, M):
     """act as the gate/up stage leaves it in the workspace (the header's layout)."""
-    if fmt == "nvfp4w8":                            # W4A8: x codes, x scales, then act float32
-        off, n, dt = a256(M * H) + a256(M * 4), M * I * 4, np.float32
+    if fmt == "nvfp4w8":                            # W4A8: x's E4M3 values (float16), x scales, then act float32
+        off, n, dt = a256(M * H * 2) + a256(M * 4), M * I * 4, np.float32
     elif path == "gemv":
         off, n, dt = 0, M * I * (4 if fmt == "fp8" else 2), (np.float32 if fmt == "fp8" else np.float16)
     elif fmt == "fp8":

@@ -31,21 +31,25 @@ def a256(n):
     return -(-n // 256) * 256
 
 
-def unsplit(q):
-    """Device code order [k0 k2 k4 k6 | k1 k3 k5 k7] per 8 k -> natural k order."""
-    q = np.asarray(q).reshape(q.shape[0], -1, 2, 4)
-    nat = np.empty(q.shape[:2] + (8,), dtype=q.dtype)
-    nat[:, :, 0::2] = q[:, :, 0, :]
-    nat[:, :, 1::2] = q[:, :, 1, :]
-    return nat.reshape(q.shape[0], -1)
+def codes_of(q16):
+    """The device's quantized rows (float16 bits, each an E4M3 value) -> their E4M3 codes.  Asserts that every
+    value is exactly an E4M3 value (sign of zero included), so comparing codes compares the values."""
+    v = np.asarray(q16).view(np.float16).astype(np.float64)
+    codes = oracle.e4m3_encode_rne(v)
+    back = oracle.codecs.e4m3_to_f64(codes)
+    nan = np.isnan(v)
+    assert np.array_equal(np.isnan(back), nan), "a NaN does not round-trip"
+    same = (back == v) & (np.signbit(back) == np.signbit(v))
+    assert np.all(same | nan), "a quantized value is not an E4M3 value"
+    return codes
 
 
 def ws_regions(M, Hh, Ii):
     xq = 0
-    sx = a256(M * Hh)
+    sx = a256(M * Hh * 2)
     act = sx + a256(M * 4)
     aq = act + a256(M * Ii * 4)
-    sa = aq + a256(M * Ii)
+    sa = aq + a256(M * Ii * 2)
     return dict(xq=xq, sx=sx, act=act, aq=aq, sa=sa)
 
 
@@ -65,7 +69,7 @@ def check_w4a8(y, ws, x64, blk_args, rows, Hh, Ii, M, what):
     """
     R = ws_regions(M, Hh, Ii)
     act = view(ws, R["act"], M * Ii, np.float32, (M, Ii))[rows]
-    aq = unsplit(view(ws, R["aq"], M * Ii, np.uint8, (M, Ii)))[rows]
+    aq = codes_of(view(ws, R["aq"], M * Ii, np.uint16, (M, Ii)))[rows]
     sa = view(ws, R["sa"], M, np.float32, (M,))[rows].astype(np.float64)
     own_q, own_s = oracle.quant_e4m3_per_token(act.astype(np.float64))
     assert np.array_equal(sa, own_s) and np.array_equal(aq, own_q), f"{what}: act codes"
@@ -129,7 +133,7 @@ def test_x_codes_and_scales_bit_exact(nv_small, xdt):
     wq.mlp_nvfp4_run(xt, *nv_args(blk, W), workspace=ws, stage="gateup", act="e4m3")
     torch.cuda.synchronize()
     R = ws_regions(M, Hh, Ii)
-    q = unsplit(view(ws, R["xq"], M * Hh, np.uint8, (M, Hh)))
+    q = codes_of(view(ws, R["xq"], M * Hh, np.uint16, (M, Hh)))
     s = view(ws, R["sx"], M, np.float32, (M,))
     wq_codes, wq_scale = oracle.quant_e4m3_per_token(x64)
     assert np.array_equal(s.astype(np.float64), wq_scale)
@@ -201,10 +205,10 @@ def test_ragged_and_short(nv_small, M):
                f"w4a8 M={M} 512x1024")
 
 
-@pytest.mark.parametrize("N,K", [(67, 384), (45, 256), (130, 640)])
+@pytest.mark.parametrize("N,K", [(67, 384), (45, 256), (130, 640), (67, 320)])
 def test_linear_tail_shapes(N, K):
-    # the NVFP4 page's tail case has 129 rows and 67 output rows; K here is a multiple of 128 (the variant's
-    # K step), with an odd number of steps (a short last weight block) at 384 and 640
+    # the NVFP4 page's tail case has 129 rows and 67 output rows; K is a multiple of 64 (one record) and at
+    # least 256 (one weight block of four records), with a short last weight block at 320, 384 and 640
     wp, ws, gs = synth.nvfp4_tensor(N, K, 3, 44)
     blk = oracle.block64_pack(wp, ws)
     x = np.random.default_rng(N + K).standard_normal((129, K)).astype(np.float32)
@@ -222,5 +226,5 @@ def test_rejected_forms(nv_small):
     assert wq.mlp_workspace_bytes(wq.WQ_FMT_FP8W, 4, 256, 256, "auto", "e4m3") == 0
     xs = dev(np.zeros((4, 192), np.float32))
     wp, ws_, gs = synth.nvfp4_tensor(64, 192, 3, 46)
-    with pytest.raises(wq.WQError):                       # K = 192 is not a multiple of 128
+    with pytest.raises(wq.WQError):                       # K = 192 is below one weight block (256)
         wq.qlinear_run(wq.WQ_FMT_NVFP4, xs, dev(oracle.block64_pack(wp, ws_)), None, float(gs), act="e4m3")

@@ -145,8 +145,8 @@ int linear_path(int fmt, int64_t M, int64_t N, int64_t K, int flags) {
   if (flags & WQ_ACT_E4M3) return WQ_PATH_MFMA;
   return pick_path(fmt, M, N, K, wbytes(fmt, N, K), flags);
 }
-// A dimension the W4A8 GEMM takes as K: whole 128-wide steps, at least two.
-bool w8_k_ok(int64_t K) { return K % 128 == 0 && K >= 256; }
+// A dimension the W4A8 GEMMs take as K: whole 64-wide steps (Block64 records), at least four (one weight block).
+bool w8_k_ok(int64_t K) { return K % 64 == 0 && K >= 256; }
 
 // Split-K scratch of the MFMA path: gate+up and down run one after the other and share it.
 size_t mlp_partials(int fmt, int64_t M, int64_t H, int64_t I) {
@@ -187,9 +187,10 @@ MfmaWs mfma_ws(int fmt, int64_t M, int64_t H, int64_t I) {
   return w;
 }
 
-// Workspace regions of the W4A8 variant (each 256-byte aligned, in this order): xq [M,H] E4M3 codes of x,
-// sx [M] float32 (x row scales), act32 [M,I] float32, aq [M,I] E4M3 codes of act, sa [M] float32 (act row
-// scales), then the split-K partial tiles of the larger of the two GEMMs.
+// Workspace regions of the W4A8 variant (each 256-byte aligned, in this order): xq [M,H] float16 holding
+// the E4M3 values of x's rows (scaled by their row scale's inverse), sx [M] float32 (x row scales), act32
+// [M,I] float32, aq [M,I] float16 holding the E4M3 values of act's rows, sa [M] float32 (act row scales),
+// then the split-K partial tiles of the larger of the two GEMMs.
 struct W8Ws {
   size_t xq, sx, act32, aq, sa, partials, total;
 };
@@ -197,13 +198,13 @@ W8Ws w8_ws(int64_t M, int64_t H, int64_t I) {
   W8Ws w{};
   size_t o = 0;
   w.xq = o;
-  o += align256((size_t)M * H);
+  o += align256((size_t)M * H * 2);
   w.sx = o;
   o += align256((size_t)M * 4);
   w.act32 = o;
   o += align256((size_t)M * I * 4);
   w.aq = o;
-  o += align256((size_t)M * I);
+  o += align256((size_t)M * I * 2);
   w.sa = o;
   o += align256((size_t)M * 4);
   w.partials = o;
@@ -326,10 +327,10 @@ int mlp_run(int fmt, int64_t M, int64_t H, int64_t I, const void* x, int x_dtype
   if (w8) {
     // W4A8: x quantized per token once for gate and up; act (float32) quantized the same way for down
     const W8Ws L = w8_ws(M, H, I);
-    uint8_t* xq = base + L.xq;
+    uint16_t* xq = reinterpret_cast<uint16_t*>(base + L.xq);
     float* sx = reinterpret_cast<float*>(base + L.sx);
     float* act32 = reinterpret_cast<float*>(base + L.act32);
-    uint8_t* aq = base + L.aq;
+    uint16_t* aq = reinterpret_cast<uint16_t*>(base + L.aq);
     float* sa = reinterpret_cast<float*>(base + L.sa);
     float* partials = L.total > L.partials ? reinterpret_cast<float*>(base + L.partials) : nullptr;
     if (do_gu) {
@@ -531,7 +532,7 @@ size_t qlinear_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K, int fla
   if (M <= 0 || N <= 0 || K <= 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim || !elems_ok(M, N, K)) return 0;
   if (flags & WQ_ACT_E4M3) {
     if (fmt != WQ_FMT_NVFP4 || (flags & 3) == WQ_PATH_GEMV || !w8_k_ok(K)) return 0;
-    return align256((size_t)M * K) + align256((size_t)M * 4) + align256(wq::w4a8_partial_bytes((int)M, (int)K, (int)N, false));
+    return align256((size_t)M * K * 2) + align256((size_t)M * 4) + align256(wq::w4a8_partial_bytes((int)M, (int)K, (int)N, false));
   }
   if (linear_path(fmt, M, N, K, flags) == WQ_PATH_GEMV) return 0;
   return align256((size_t)M * K * 2) + align256((size_t)M * 4) +
@@ -582,11 +583,11 @@ int qlinear_run(int fmt, int64_t M, int64_t N, int64_t K, const void* x, int x_d
     return launched(wq::launch_nvfp4_gemv((int)M, (int)K, (int)N, x, xt, w, inv, nullptr, 0.f, y, false, st));
   }
   uint8_t* base = reinterpret_cast<uint8_t*>(workspace);
-  if (w8) {   // workspace: xq [M,K] E4M3 codes, sx [M], partials
-    uint8_t* xq = base;
-    float* sx = reinterpret_cast<float*>(base + align256((size_t)M * K));
+  if (w8) {   // workspace: xq [M,K] float16 (E4M3 values), sx [M], partials
+    uint16_t* xq = reinterpret_cast<uint16_t*>(base);
+    float* sx = reinterpret_cast<float*>(base + align256((size_t)M * K * 2));
     float* partials = wq::w4a8_partial_bytes((int)M, (int)K, (int)N, false)
-                          ? reinterpret_cast<float*>(base + align256((size_t)M * K) + align256((size_t)M * 4))
+                          ? reinterpret_cast<float*>(base + align256((size_t)M * K * 2) + align256((size_t)M * 4))
                           : nullptr;
     rc = launched(wq::launch_quant_e4m3((int)M, (int)K, x, xt, xq, sx, st));
     if (rc == WQ_OK) rc = launched(wq::launch_w4a8_linear((int)M, (int)K, (int)N, xq, sx, w, inv, y, partials, st));

@@ -79,16 +79,17 @@ hipError_t launch_mfma_linear(int fmt, int M, int K, int N, const uint16_t* a16,
                               hipStream_t st);
 
 // ---- W4A8: NVFP4 weights x per-token E4M3 activations (MFMA) --------------------------------------
-// x [M,K] (f32 or bf16) -> q [M,K] E4M3 codes (each 8 k stored as k0 k2 k4 k6 k1 k3 k5 k7), rowscale[m] =
-// 2^e with max_k |x[m,k]| * 2^-e in (224, 448]; K a multiple of 8.
-hipError_t launch_quant_e4m3(int M, int K, const void* x, XType xt, uint8_t* q, float* rowscale, hipStream_t st);
-// GEMMs on those codes and Block64 weights (K a multiple of 128, at least 256): gate+up writes act =
-// silu(g) * u as float32 [M,N] with g = rowscale[m] * inv0 * acc; the single matrix writes y [M,N].
-// partials: float32 scratch of w4a8_partial_bytes(M, K, N, gu) bytes (NULL allowed when that is 0).
+// x [M,K] (f32 or bf16) -> q [M,K] float16 holding the E4M3 values of x[m,k] * 2^-e (round to nearest
+// even), rowscale[m] = 2^e with max_k |x[m,k]| * 2^-e in (224, 448]; K a multiple of 8.
+hipError_t launch_quant_e4m3(int M, int K, const void* x, XType xt, uint16_t* q, float* rowscale, hipStream_t st);
+// GEMMs on those values and Block64 weights (the float16 path's GEMM; K a multiple of 64, at least 256):
+// gate+up writes act = silu(g) * u as float32 [M,N] with g = rowscale[m] * inv0 * acc; the single matrix
+// writes y [M,N].  partials: float32 scratch of w4a8_partial_bytes(M, K, N, gu) bytes (NULL allowed when
+// that is 0).
 size_t w4a8_partial_bytes(int M, int K, int N, bool gu);
-hipError_t launch_w4a8_gateup(int M, int K, int N, const uint8_t* xq, const float* sx, const uint8_t* w0, float inv0,
+hipError_t launch_w4a8_gateup(int M, int K, int N, const uint16_t* xq, const float* sx, const uint8_t* w0, float inv0,
                               const uint8_t* w1, float inv1, float* act, float* partials, hipStream_t st);
-hipError_t launch_w4a8_linear(int M, int K, int N, const uint8_t* aq, const float* sa, const uint8_t* w, float inv,
+hipError_t launch_w4a8_linear(int M, int K, int N, const uint16_t* aq, const float* sa, const uint8_t* w, float inv,
                               float* y, float* partials, hipStream_t st);
 
 // ---- AWQ routed-expert single-token step ------------------------------------------------------

@@ -503,7 +503,9 @@ inline size_t nv_partial_bytes(const NvPlan& p, bool gu) {
 // FMT 1: NVFP4 Block64 weights, column factor inv0 / inv1.  FMT 0: FP8 E4M3 codes [N][K], column scales
 // cs0[n] / cs1[n].  ABF (FMT 0 only): a16 holds bfloat16 activations as given (no row scale) and the
 // MFMAs run on bf16 operands (E4M3 codes decode to bf16 exactly); otherwise both operands are f16.
-template <int FMT, bool GU, int MB, bool BS, bool ABF>
+// A32 (gate+up): act is stored as float32 (FP8, whose definition keeps act unrounded, and the W4A8 variant,
+// which quantizes it per token next), else as float16.
+template <int FMT, bool GU, int MB, bool BS, bool ABF, bool A32>
 __global__ void __launch_bounds__(256, 2) nv_gemm_kernel(int M, int K, int N, NvPlan plan,
                                                         const uint16_t* __restrict__ a16,
                                                         const float* __restrict__ rowscale,
@@ -891,7 +893,7 @@ __global__ void __launch_bounds__(256, 2) nv_gemm_kernel(int M, int K, int N, Nv
           const float g = acc[0][mb][r] * rs * c0;
           const float u = acc[1][mb][r] * rs * c1;
           const float a = silu_f32(g) * u;
-          if constexpr (FMT == 0) reinterpret_cast<float*>(out)[(size_t)m * N + ncol] = a;   // FP8: float32 act
+          if constexpr (A32) reinterpret_cast<float*>(out)[(size_t)m * N + ncol] = a;
           else reinterpret_cast<uint16_t*>(out)[(size_t)m * N + ncol] = __builtin_bit_cast(uint16_t, (_Float16)a);
         } else {
           reinterpret_cast<float*>(out)[(size_t)m * N + ncol] = acc[0][mb][r] * rs * c0;
@@ -993,18 +995,18 @@ __global__ void __launch_bounds__(256) nv_splitk_finish(int M, int N, NvPlan pla
   }
 }
 
-template <int FMT, bool GU, int MB, bool BS, bool ABF>
+template <int FMT, bool GU, int MB, bool BS, bool ABF, bool A32>
 hipError_t nv_launch(int M, int K, int N, const NvPlan& plan, const uint16_t* a16, const float* rowscale,
                      const uint8_t* w0, const float* cs0, float inv0, const uint8_t* w1, const float* cs1,
                      float inv1, void* out, float* partials, hipStream_t st) {
-  if (!raise_lds_limit<nv_gemm_kernel<FMT, GU, MB, BS, ABF>>()) return hipErrorInvalidValue;   // up to 72 KB
+  if (!raise_lds_limit<nv_gemm_kernel<FMT, GU, MB, BS, ABF, A32>>()) return hipErrorInvalidValue;   // up to 72 KB
   const int grid = plan.units_grid + (plan.full + 7) / 8 * 8;
-  hipLaunchKernelGGL((nv_gemm_kernel<FMT, GU, MB, BS, ABF>), dim3(grid), dim3(256), g_lds_bytes<FMT>(GU, MB, BS), st, M,
+  hipLaunchKernelGGL((nv_gemm_kernel<FMT, GU, MB, BS, ABF, A32>), dim3(grid), dim3(256), g_lds_bytes<FMT>(GU, MB, BS), st, M,
                      K, N, plan, a16, rowscale, w0, cs0, inv0, w1, cs1, inv1, out, partials);
   return hipGetLastError();
 }
 
-template <int FMT, bool GU, bool ABF>
+template <int FMT, bool GU, bool ABF, bool A32 = (FMT == 0)>
 hipError_t nv_dispatch(int M, int K, int N, const uint16_t* a16, const float* rowscale, const uint8_t* w0,
                        const float* cs0, float inv0, const uint8_t* w1, const float* cs1, float inv1, void* out,
                        float* partials, hipStream_t st) {
@@ -1014,17 +1016,17 @@ hipError_t nv_dispatch(int M, int K, int N, const uint16_t* a16, const float* ro
   hipError_t e;
   switch (plan.bm) {
     case 32:
-      e = nv_launch<FMT, GU, 1, true, ABF>(M, K, N, plan, a16, rowscale, w0, cs0, inv0, w1, cs1, inv1, out, partials, st);
+      e = nv_launch<FMT, GU, 1, true, ABF, A32>(M, K, N, plan, a16, rowscale, w0, cs0, inv0, w1, cs1, inv1, out, partials, st);
       break;
     case 64:
-      e = nv_launch<FMT, GU, 2, false, ABF>(M, K, N, plan, a16, rowscale, w0, cs0, inv0, w1, cs1, inv1, out, partials, st);
+      e = nv_launch<FMT, GU, 2, false, ABF, A32>(M, K, N, plan, a16, rowscale, w0, cs0, inv0, w1, cs1, inv1, out, partials, st);
       break;
     default:
-      e = nv_launch<FMT, GU, 4, false, ABF>(M, K, N, plan, a16, rowscale, w0, cs0, inv0, w1, cs1, inv1, out, partials, st);
+      e = nv_launch<FMT, GU, 4, false, ABF, A32>(M, K, N, plan, a16, rowscale, w0, cs0, inv0, w1, cs1, inv1, out, partials, st);
       break;
   }
   if (e != hipSuccess || plan.units == 0) return e;
-  hipLaunchKernelGGL((nv_splitk_finish<GU, GU && FMT == 0>), dim3((plan.tiles - plan.full) * nv_finish_per_tile(M, plan)),
+  hipLaunchKernelGGL((nv_splitk_finish<GU, GU && A32>), dim3((plan.tiles - plan.full) * nv_finish_per_tile(M, plan)),
                      dim3(256), 0, st, M, N,
                      plan, partials, rowscale, cs0, inv0, cs1, inv1, out);
   return hipGetLastError();
@@ -1054,40 +1056,35 @@ hipError_t gemm_dispatch(int M, int K, int N, const uint16_t* a16, const float* 
 //
 // Activation quantization (page "Qwen3.8-27B-NVFP4", section "Implemented execution path": per-token
 // dynamic 8-bit activations in a small workspace, one quantization of x shared by gate and up): each row
-// is scaled by the power of two 2^-e that puts its largest magnitude in (224, 448] (exact) and encoded
-// to E4M3 with round to nearest even (v_cvt_pk_fp8_f32).  The codes of each 8 consecutive k are stored
-// as [k0 k2 k4 k6 | k1 k3 k5 k7], the order in which the weight decode below produces its bytes, so the
-// two MFMA operands pair the same k (an MFMA sums over its 16 k in any order).
-//
-// GEMM: one K = 16 E4M3 MFMA per E4M3 weight group (v_mfma_f32_32x32x16_fp8_fp8), each lane holding
-// k = 16 g + 8 h + j of the group; its float32 partial is scaled by the group's E4M3 scale (one value per
-// lane: every D register of a lane belongs to the lane's weight column) and added to the accumulator.
-// E2M1 codes become E4M3 bytes exactly (same values; the group scale is not folded in: E2M1 x E4M3 needs
-// more significand bits than E4M3 has).  K steps are 128 wide (the activation tile keeps 128-byte rows),
-// weight blocks hold 4 records (two K steps); copies, split-K plan and finish are those of nv_gemm_kernel.
-
-// E4M3 code of a row's exponent e: smallest e with amax <= 448 * 2^e (amax = f 2^p, f in [0.5, 1):
-// 448 = 0.875 * 2^9, so e = p - 9, plus one when f > 0.875); 0 for a zero or non-finite amax.
+// is scaled by the power of two 2^-e that puts its largest magnitude in (224, 448] (exact) and rounded to
+// E4M3 with round to nearest even (v_cvt_pk_fp8_f32).  Every E4M3 value is a float16, so the quantized
+// row is stored as float16 values (the code's value, exactly) and the GEMMs are the float16 path's own:
+// its decoded weights (E2M1 x E4M3 group scale) are exact float16 values too, so each MFMA product is the
+// exact product of a quantized activation and a weight, accumulated in float32, and 2^e is the row scale
+// its epilogue already applies.  (A form with one K = 16 fp8 MFMA per weight group and a float32 rescale
+// of each group's result took 0.45 ms at M = 512 against 0.29 ms for this one: the rescale costs 16 FMAs
+// per lane per MFMA.)
+// E4M3 exponent of a row: smallest e with amax <= 448 * 2^e (amax = f 2^p, f in [0.5, 1): 448 = 0.875 * 2^9,
+// so e = p - 9, plus one when f > 0.875); 0 for a zero or non-finite amax.
 __device__ __forceinline__ int e4m3_token_exp(float amax) {
   if (!(amax > 0.f) || !(amax <= 3.0e38f)) return 0;
   int p;
   const float f = frexpf(amax, &p);
   return p - 9 + (f > 0.875f ? 1 : 0);
 }
-
-// 8 consecutive elements (as float32) -> 8 E4M3 codes in [k0 k2 k4 k6 | k1 k3 k5 k7] order, scaled by 2^-e.
-__device__ __forceinline__ u32x2 e4m3_pack8_split(const float* v, int e) {
+// 8 consecutive elements (as float32) scaled by 2^-e -> their E4M3 values as 8 float16 (16 bytes, in order).
+__device__ __forceinline__ u32x4 e4m3_round8_f16(const float* v, int e) {
   float s[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) s[j] = ldexpf(v[j], -e);
   int lo = 0, hi = 0;
-  lo = __builtin_amdgcn_cvt_pk_fp8_f32(s[0], s[2], lo, false);
-  lo = __builtin_amdgcn_cvt_pk_fp8_f32(s[4], s[6], lo, true);
-  hi = __builtin_amdgcn_cvt_pk_fp8_f32(s[1], s[3], hi, false);
-  hi = __builtin_amdgcn_cvt_pk_fp8_f32(s[5], s[7], hi, true);
-  return u32x2{(uint32_t)lo, (uint32_t)hi};
+  lo = __builtin_amdgcn_cvt_pk_fp8_f32(s[0], s[1], lo, false);
+  lo = __builtin_amdgcn_cvt_pk_fp8_f32(s[2], s[3], lo, true);
+  hi = __builtin_amdgcn_cvt_pk_fp8_f32(s[4], s[5], hi, false);
+  hi = __builtin_amdgcn_cvt_pk_fp8_f32(s[6], s[7], hi, true);
+  return u32x4{as_u32(e4m3x2_f16<false>((uint32_t)lo)), as_u32(e4m3x2_f16<true>((uint32_t)lo)),
+               as_u32(e4m3x2_f16<false>((uint32_t)hi)), as_u32(e4m3x2_f16<true>((uint32_t)hi))};
 }
-
 template <typename XT>
 __device__ __forceinline__ void load8(const XT* row, int u, float* v) {
   if constexpr (std::is_same<XT, float>::value) {
@@ -1106,12 +1103,11 @@ __device__ __forceinline__ void load8(const XT* row, int u, float* v) {
     }
   }
 }
-
 // One 256-thread workgroup per row; units of 8 elements, RU of them per thread kept in registers (the
-// rest read again).  rowscale[m] = 2^e; codes [M][K] bytes.
+// rest read again).  q [M][K] float16 (E4M3 values); rowscale[m] = 2^e.
 template <typename XT, int RU>
 __global__ void __launch_bounds__(256) quant_e4m3_kernel(int M, int K, const XT* __restrict__ x,
-                                                         uint8_t* __restrict__ q, float* __restrict__ rowscale) {
+                                                         uint16_t* __restrict__ q, float* __restrict__ rowscale) {
   __shared__ float wmax[4];
   const int m = (int)blockIdx.x;
   const int t = (int)threadIdx.x;
@@ -1141,318 +1137,17 @@ __global__ void __launch_bounds__(256) quant_e4m3_kernel(int M, int K, const XT*
   amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
   const int e = e4m3_token_exp(amax);
   if (t == 0) rowscale[m] = ldexpf(1.0f, e);
-  u32x2* o = reinterpret_cast<u32x2*>(q + (size_t)m * K);
+  u32x4* o = reinterpret_cast<u32x4*>(q + (size_t)m * K);
 #pragma unroll
   for (int i = 0; i < RU; ++i) {
     const int u = t + 256 * i;
-    if (u < nu) o[u] = e4m3_pack8_split(cache[i], e);
+    if (u < nu) o[u] = e4m3_round8_f16(cache[i], e);
   }
   for (int u = t + 256 * RU; u < nu; u += 256) {
     float v[8];
     load8<XT>(row, u, v);
-    o[u] = e4m3_pack8_split(v, e);
+    o[u] = e4m3_round8_f16(v, e);
   }
-}
-
-// 8 E2M1 codes (k = 0..7 of a dword, low nibble first) -> their E4M3 bytes as [k0 k2 k4 k6 | k1 k3 k5 k7]:
-// the 3-bit magnitude indexes a byte table of the 8 E2M1 magnitudes in E4M3 (0, 0.5, 1, 1.5, 2, 3, 4, 6 =
-// 0x00 0x30 0x38 0x3C 0x40 0x44 0x48 0x4C) through v_perm_b32, and the sign moves from bit 3 to bit 7.
-__device__ __forceinline__ long e2m1x8_e4m3_split(uint32_t w) {
-  constexpr uint32_t kLo = 0x3C383000u, kHi = 0x4C484440u;
-  const uint32_t ev = w & 0x0F0F0F0Fu, od = (w >> 4) & 0x0F0F0F0Fu;
-  const uint32_t a = __builtin_amdgcn_perm(kHi, kLo, ev & 0x07070707u) | ((ev & 0x08080808u) << 4);
-  const uint32_t b = __builtin_amdgcn_perm(kHi, kLo, od & 0x07070707u) | ((od & 0x08080808u) << 4);
-  return (long)(((uint64_t)b << 32) | a);
-}
-
-constexpr int kW8KSB = 2;       // 128-wide K steps per weight block (4 records)
-constexpr int kW8Min = 256;     // smallest K (the short last block is read as the row's last 144 bytes)
-
-// Tile rows / 32 of the W4A8 GEMM: 32- or 64-row tiles (stepped schedule only).  The per-group partials
-// and their rescale need the registers that a 128-row tile's accumulators would take.
-inline int w8_mb(int M) { return M <= 32 ? 1 : 2; }
-inline NvPlan w8_plan(int M, int K, int N, bool gu) {
-  return nv_plan_ex(M, K, N, gu, 2 * kW8KSB, kNvSlots, 8, w8_mb(M));
-}
-
-template <bool GU, int MB>
-__global__ void __launch_bounds__(256, 2) w4a8_gemm_kernel(int M, int K, int N, NvPlan plan,
-                                                          const uint8_t* __restrict__ aq,
-                                                          const float* __restrict__ rowscale,
-                                                          const uint8_t* __restrict__ w0, float inv0,
-                                                          const uint8_t* __restrict__ w1, float inv1,
-                                                          void* __restrict__ out, float* __restrict__ partials) {
-  using Geo = WGeo<1>;
-  constexpr int CB = Geo::CB, CPM = Geo::CPM, MBYTES = Geo::MBYTES;
-  constexpr int KSB = kW8KSB;
-  constexpr int NM = GU ? 2 : 1;
-  constexpr int kAStage = nv_astage(MB);        // 32 MB rows x 128 bytes
-  constexpr int PT = 32 * MB * 128;
-  constexpr int NW = NM * CPM;
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  const int nk = K >> 7;                        // 128-wide K steps
-  const int nblk = (nk + KSB - 1) / KSB;
-  const int b = (int)blockIdx.x;
-  int tile, part = -1, kb0 = 0, kb1 = nblk;
-  if (b < plan.units_grid) {
-    if (b >= plan.units) return;
-    tile = plan.full + b / plan.S;
-    part = b - (b / plan.S) * plan.S;
-    kb0 = part * plan.bps;
-    kb1 = min(kb0 + plan.bps, nblk);
-  } else {
-    const int f = b - plan.units_grid;
-    const int per = ((int)gridDim.x - plan.units_grid) >> 3;
-    tile = (f & 7) * per + (f >> 3);
-    if (tile >= plan.full) return;
-  }
-  const int kt0 = KSB * kb0, kt1 = min(KSB * kb1, nk);
-  const int tm = tile / plan.ntn;
-  const int tn = tile - tm * plan.ntn;
-  const int m0 = tm * 32 * MB;
-  const int n0 = tn * 128;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int li = lane & 31;
-  const int h = lane >> 5;
-  const uint32_t rb = (uint32_t)(K >> 6) * 36u;  // bytes per weight row
-  const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
-  const uint32_t wlds = lds0 + 2 * kAStage + wave * NM * MBYTES;
-  const uint8_t* wbuf = lds + 2 * kAStage + wave * NM * MBYTES;
-
-  // activation codes: tile row p >> 3, LDS chunk p & 7 holds global chunk (p & 7) ^ ((row >> 1) & 7) of the step
-  const uint8_t* a_tile = aq + (size_t)m0 * K;
-  uint32_t aoff[MB];
-#pragma unroll
-  for (int i = 0; i < MB; ++i) {
-    const int p = tid + 256 * i, row = p >> 3, c = p & 7;
-    aoff[i] = (uint32_t)(min(m0 + row, M - 1) - m0) * (uint32_t)K + (uint32_t)((c ^ ((row >> 1) & 7)) * 16);
-  }
-  const int nw0 = min(n0 + 32 * wave, N - 1);
-  const uint8_t* wbase0 = w0 + (size_t)nw0 * rb;
-  const uint8_t* wbase1 = GU ? w1 + (size_t)nw0 * rb : wbase0;
-  uint32_t woff[NW];
-#pragma unroll
-  for (int j = 0; j < NW; ++j) {
-    int s = 64 * (j % CPM) + lane;
-    if (s >= 288) s -= 288;
-    const int c = s / 9, q = s - 9 * c;
-    woff[j] = (uint32_t)(min(n0 + 32 * wave + c, N - 1) - nw0) * rb + 16u * (uint32_t)q;
-  }
-  auto copy_a = [&](int kt, int stage) {
-    kt = min(kt, nk - 1);
-    const uint8_t* base = a_tile + (size_t)kt * 128;
-    const uint32_t sb = lds0 + stage * kAStage;
-#pragma unroll
-    for (int i = 0; i < MB; ++i)
-      lds_copy16(aoff[i], base, __builtin_amdgcn_readfirstlane(sb + (256 * i + 64 * wave) * 16));
-  };
-  const int rtail = nk % KSB;
-  auto copy_w = [&](int blk) {
-    blk = min(blk, nblk - 1);
-    const uint32_t boff = (rtail && blk == nblk - 1) ? rb - (uint32_t)CB : (uint32_t)blk * CB;
-    // runs of up to four copies, each run with one M0 write (copy j lands at wlds + 1024 j)
-    uint32_t v[NW];
-    const uint8_t* bases[NW];
-#pragma unroll
-    for (int j = 0; j < NW; ++j) {
-      v[j] = woff[j] + boff;
-      bases[j] = (j < CPM ? wbase0 : wbase1) - 1024 * (j & 3);
-    }
-#pragma unroll
-    for (int g = 0; g < NW; g += 4) {
-      const uint32_t lb = __builtin_amdgcn_readfirstlane(wlds + 1024 * g);
-      if (g + 4 <= NW) lds_copy16_run<4>(v + g, bases + g, lb);
-      else lds_copy16_run<(NW % 4 == 0 ? 4 : NW % 4)>(v + g, bases + g, lb);
-    }
-  };
-
-  f32x16 acc[NM][MB];
-#pragma unroll
-  for (int t = 0; t < NM; ++t)
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[t][mb][r] = 0.f;
-
-  // One weight block of this lane's column of matrix t: record R's scale dword and, for each of its 4
-  // groups, the 4 code bytes of half h (k = 16 g + 8 h .. + 7).
-  struct WB { uint32_t nib[4][4]; uint32_t d[4]; };
-  auto read_block = [&](WB* wb, int blk) {
-#pragma unroll
-    for (int t = 0; t < NM; ++t) {
-      const uint8_t* bp = wbuf + MBYTES * t + 144 * li;
-#pragma unroll
-      for (int R = 0; R < 4; ++R) {
-        wb[t].d[R] = *reinterpret_cast<const uint32_t*>(bp + 36 * R);
-#pragma unroll
-        for (int g = 0; g < 4; ++g) wb[t].nib[R][g] = *reinterpret_cast<const uint32_t*>(bp + 36 * R + 4 + 8 * g + 4 * h);
-      }
-    }
-    if (rtail && blk == nblk - 1) {             // the short last block's step sits at position 1
-#pragma unroll
-      for (int t = 0; t < NM; ++t)
-#pragma unroll
-        for (int R = 0; R < 2; ++R) {
-          wb[t].d[R] = wb[t].d[R + 2];
-#pragma unroll
-          for (int g = 0; g < 4; ++g) wb[t].nib[R][g] = wb[t].nib[R + 2][g];
-        }
-    }
-  };
-  // the 8 codes of group s of the 128-wide step at LDS stage `stage`, rows 32 mb + li, half h
-  auto read_a = [&](int stage, int s, long* af) {
-    const uint8_t* ast = lds + stage * kAStage;
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-      af[mb] = *reinterpret_cast<const long*>(ast + (32 * mb + li) * 128 + ((s ^ ((li >> 1) & 7)) * 16) + 8 * h);
-  };
-  // group S (0..7) of step J of the block in registers: one K = 16 MFMA per (row block, matrix) into a
-  // fresh partial, each partial scaled by its group scale and added while the next MFMA runs
-  auto group = [&](const WB* wb, auto Jc, auto Sc, const long* af) {
-    constexpr int J = decltype(Jc)::value, S = decltype(Sc)::value;
-    constexpr int R = 2 * J + (S >> 2), G = S & 3, NI = MB * NM;
-    long bfr[NM];
-    float dsc[NM];
-#pragma unroll
-    for (int t = 0; t < NM; ++t) {
-      // the empty asm keeps each group's decode at its group: left free, the compiler computes every group's
-      // operands as soon as the block is read and carries them (64 registers) across the loop
-      uint32_t w = wb[t].nib[R][G], d = wb[t].d[R];
-      asm volatile("" : "+v"(w), "+v"(d));
-      bfr[t] = e2m1x8_e4m3_split(w);
-      dsc[t] = e4m3_byte_f32<0>(d >> (8 * G));
-    }
-    const f32x16 zero = {};
-    f32x16 p[2];
-    p[0] = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(af[0], bfr[0], zero, 0, 0, 0);
-#pragma unroll
-    for (int i = 1; i <= NI; ++i) {
-      if (i < NI) p[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(af[i / NM], bfr[i % NM], zero, 0, 0, 0);
-      const int j = i - 1;
-      acc[j % NM][j / NM] += p[j & 1] * dsc[j % NM];   // one fma per element (contracted)
-      // materialise the sum here: otherwise the compiler may sink the fmas of a conditional step past its
-      // end and keep every partial of the step live at once
-      asm volatile("" : "+v"(acc[j % NM][j / NM]));
-    }
-  };
-
-  WB wb[NM];
-  long af0[MB], af1[MB];
-  copy_w(kb0);
-  copy_a(kt0, 0);
-  copy_a(kt0 + 1, 1);
-  wait_vmem<MB>();
-  __syncthreads();
-  read_block(wb, kb0);
-  wait_lds();
-  copy_w(kb0 + 1);
-  read_a(0, 0, af0);
-  // sub-step S < 7: read group S+1's activation fragments, then run group S
-  auto sub = [&](auto Jc, auto Sc, int st) {
-    constexpr int S = decltype(Sc)::value;
-    if constexpr (S % 2 == 0) {
-      read_a(st, S + 1, af1);
-      group(wb, Jc, Sc, af0);
-    } else {
-      read_a(st, S + 1, af0);
-      group(wb, Jc, Sc, af1);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  auto step = [&](int kt, auto Jc) {
-    constexpr int J = decltype(Jc)::value;
-    const int st = kt & 1;
-    sub(Jc, std::integral_constant<int, 0>{}, st);
-    sub(Jc, std::integral_constant<int, 1>{}, st);
-    sub(Jc, std::integral_constant<int, 2>{}, st);
-    sub(Jc, std::integral_constant<int, 3>{}, st);
-    sub(Jc, std::integral_constant<int, 4>{}, st);
-    sub(Jc, std::integral_constant<int, 5>{}, st);
-    sub(Jc, std::integral_constant<int, 6>{}, st);
-    if constexpr (J == 0) wait_vmem<NW>();       // step kt+1's activations landed; the next block may fly
-    else wait_vmem<0>();
-    __syncthreads();
-    copy_a(kt + 2, st);
-    read_a(st ^ 1, 0, af0);
-    __builtin_amdgcn_sched_barrier(0);
-    group(wb, Jc, std::integral_constant<int, 7>{}, af1);
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr (J == KSB - 1) {
-      read_block(wb, kt / KSB + 1);
-      wait_lds();
-      copy_w(kt / KSB + 2);
-    }
-  };
-  int kt = kt0;
-  for (; kt + 1 < kt1; kt += KSB) {             // whole blocks (kt0 is even)
-    step(kt, std::integral_constant<int, 0>{});
-    step(kt + 1, std::integral_constant<int, 1>{});
-  }
-  if (kt < kt1) step(kt, std::integral_constant<int, 0>{});   // a short last block: one step
-  wait_vmem<0>();
-
-  if (part >= 0) {
-    float* pt = partials + (size_t)b * NM * PT;
-    const int col = 32 * wave + li;
-#pragma unroll
-    for (int t = 0; t < NM; ++t)
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = 32 * mb + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (m0 + row < M) pt[t * PT + row * 128 + col] = acc[t][mb][r];
-        }
-    return;
-  }
-  const int ncol = n0 + 32 * wave + li;
-  if (ncol >= N) return;
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int m = m0 + 32 * mb + 8 * (r >> 2) + 4 * h + (r & 3);
-      if (m < M) {
-        const float rs = rowscale[m];
-        if constexpr (GU) {
-          const float g = acc[0][mb][r] * rs * inv0;
-          const float u = acc[1][mb][r] * rs * inv1;
-          reinterpret_cast<float*>(out)[(size_t)m * N + ncol] = silu_f32(g) * u;
-        } else {
-          reinterpret_cast<float*>(out)[(size_t)m * N + ncol] = acc[0][mb][r] * rs * inv0;
-        }
-      }
-    }
-  }
-}
-
-template <bool GU, int MB>
-hipError_t w8_launch(int M, int K, int N, const NvPlan& plan, const uint8_t* aq, const float* rowscale,
-                     const uint8_t* w0, float inv0, const uint8_t* w1, float inv1, void* out, float* partials,
-                     hipStream_t st) {
-  if (!raise_lds_limit<w4a8_gemm_kernel<GU, MB>>()) return hipErrorInvalidValue;
-  const int grid = plan.units_grid + (plan.full + 7) / 8 * 8;
-  const int lds = 2 * nv_astage(MB) + 4 * (GU ? 2 : 1) * WGeo<1>::MBYTES;
-  hipLaunchKernelGGL((w4a8_gemm_kernel<GU, MB>), dim3(grid), dim3(256), lds, st, M, K, N, plan, aq, rowscale, w0, inv0,
-                     w1, inv1, out, partials);
-  return hipGetLastError();
-}
-
-template <bool GU>
-hipError_t w8_dispatch(int M, int K, int N, const uint8_t* aq, const float* rowscale, const uint8_t* w0, float inv0,
-                       const uint8_t* w1, float inv1, float* out, float* partials, hipStream_t st) {
-  if (K < kW8Min || K % 128) return hipErrorInvalidValue;
-  const NvPlan plan = w8_plan(M, K, N, GU);
-  if (plan.units > 0 && partials == nullptr) return hipErrorInvalidValue;
-  hipError_t e;
-  if (plan.bm == 32) e = w8_launch<GU, 1>(M, K, N, plan, aq, rowscale, w0, inv0, w1, inv1, out, partials, st);
-  else e = w8_launch<GU, 2>(M, K, N, plan, aq, rowscale, w0, inv0, w1, inv1, out, partials, st);
-  if (e != hipSuccess || plan.units == 0) return e;
-  hipLaunchKernelGGL((nv_splitk_finish<GU, true>), dim3((plan.tiles - plan.full) * nv_finish_per_tile(M, plan)),
-                     dim3(256), 0, st, M, N, plan, partials, rowscale, nullptr, inv0, nullptr, inv1, out);
-  return hipGetLastError();
 }
 
 }  // namespace
@@ -1522,7 +1217,7 @@ hipError_t launch_mfma_linear(int fmt, int M, int K, int N, const uint16_t* a16,
 
 namespace wq {
 
-hipError_t launch_quant_e4m3(int M, int K, const void* x, XType xt, uint8_t* q, float* rowscale, hipStream_t st) {
+hipError_t launch_quant_e4m3(int M, int K, const void* x, XType xt, uint16_t* q, float* rowscale, hipStream_t st) {
   if (K % 8) return hipErrorInvalidValue;
   // units of 8 per thread kept in registers: 3 cover K = 6144, 9 cover K = 18432
   if (xt == X_BF16) {
@@ -1541,19 +1236,18 @@ hipError_t launch_quant_e4m3(int M, int K, const void* x, XType xt, uint8_t* q, 
   return hipGetLastError();
 }
 
-size_t w4a8_partial_bytes(int M, int K, int N, bool gu) {
-  if (K < kW8Min || K % 128 || M <= 0) return 0;
-  return nv_partial_bytes(w8_plan(M, K, N, gu), gu);
-}
+size_t w4a8_partial_bytes(int M, int K, int N, bool gu) { return mfma_partial_bytes(1, M, K, N, gu); }
 
-hipError_t launch_w4a8_gateup(int M, int K, int N, const uint8_t* xq, const float* sx, const uint8_t* w0, float inv0,
+hipError_t launch_w4a8_gateup(int M, int K, int N, const uint16_t* xq, const float* sx, const uint8_t* w0, float inv0,
                               const uint8_t* w1, float inv1, float* act, float* partials, hipStream_t st) {
-  return w8_dispatch<true>(M, K, N, xq, sx, w0, inv0, w1, inv1, act, partials, st);
+  if (K < g_min_k(1)) return hipErrorInvalidValue;
+  return nv_dispatch<1, true, false, true>(M, K, N, xq, sx, w0, nullptr, inv0, w1, nullptr, inv1, act, partials, st);
 }
 
-hipError_t launch_w4a8_linear(int M, int K, int N, const uint8_t* aq, const float* sa, const uint8_t* w, float inv,
+hipError_t launch_w4a8_linear(int M, int K, int N, const uint16_t* aq, const float* sa, const uint8_t* w, float inv,
                               float* y, float* partials, hipStream_t st) {
-  return w8_dispatch<false>(M, K, N, aq, sa, w, inv, nullptr, 0.f, y, partials, st);
+  if (K < g_min_k(1)) return hipErrorInvalidValue;
+  return nv_dispatch<1, false, false, false>(M, K, N, aq, sa, w, nullptr, inv, nullptr, nullptr, 0.f, y, partials, st);
 }
 
 }  // namespace wq
