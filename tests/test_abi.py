@@ -242,6 +242,26 @@ def test_mfma_workspace_holds_the_documented_regions(L):
                 assert n > regions, (fmt, M)    # short batches split every tile along K
 
 
+def test_w4a8_workspace_holds_the_documented_regions(L):
+    # The header's W4A8 workspace (NVFP4 with WQ_ACT_E4M3): x's E4M3 values as float16 [M,H], x row scales
+    # [M], act f32 [M,I], act's E4M3 values as float16 [M,I], act row scales [M], each 256-byte aligned, then
+    # the split-K partial tiles (at most 64 MiB; none at M = 8192); 0 for FP8 or the GEMV path, and for a
+    # K that is not a multiple of 64 or is below 256.
+    H, I = 5120, 17408
+    a = lambda n: -(-n // 256) * 256
+    for M in (1, 8, 32, 64, 129, 512, 8192):
+        regions = a(M * H * 2) + a(M * 4) + a(M * I * 4) + a(M * I * 2) + a(M * 4)
+        n = wq.mlp_workspace_bytes(1, M, H, I, "auto", "e4m3")
+        assert regions <= n <= regions + (64 << 20) and n % 256 == 0, M
+        if M == 8192:
+            assert n == regions
+    assert wq.mlp_workspace_bytes(0, 8, H, I, "auto", "e4m3") == 0
+    assert wq.mlp_workspace_bytes(1, 8, H, I, "gemv", "e4m3") == 0
+    assert wq.mlp_workspace_bytes(1, 8, 320, 512, "auto", "e4m3") > 0      # K = 320: a multiple of 64
+    assert wq.mlp_workspace_bytes(1, 8, 192, 512, "auto", "e4m3") == 0     # K = 192: below 256
+    assert wq.mlp_workspace_bytes(1, 8, 288, 512, "auto", "e4m3") == 0     # K = 288: not a multiple of 64
+
+
 def test_binding_stage_calls_need_a_workspace():
     # a one-stage call hands act to the other stage through the caller's workspace; without one the
     # binding raises before touching the device (CPU tensors here never reach the library)
