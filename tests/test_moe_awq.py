@@ -138,9 +138,10 @@ def test_rotating_ids_and_determinism(moe):
         check_act_bound(d, act, ref_act, ids)
 
 
-# Shapes reaching every kernel form of the step: W2 row-pair kernel with 1..4 groups per half row
-# (I = 32 .. 256), the piece kernel (I = 320, 512) and the per-row kernel (I = 1024); W13 with 1..8
-# groups per lane (H = 256 .. 4096) and its runtime loop (H = 8192); top-k 1, 3, 16.
+# Shapes reaching every kernel form of the step: the W2 row-part kernel with two lanes per row (I = 32,
+# 64) and four lanes per row with one or two groups per lane (I = 96, 128 / 192, 256), the piece kernel
+# (I = 320, 512) and the per-row kernel (I = 1024); W13 with 1..8 groups per lane (H = 256 .. 4096) and
+# its runtime loop (H = 8192); top-k 1, 3, 16.
 MOE_SHAPES = [(24, 3, 256, 32), (24, 16, 512, 64), (24, 1, 256, 96), (40, 10, 2048, 128), (24, 5, 768, 192),
               (24, 4, 512, 256), (24, 3, 256, 320), (20, 2, 512, 512), (12, 2, 256, 1024), (12, 3, 8192, 64)]
 

@@ -181,6 +181,34 @@ __device__ __forceinline__ f16x2 awq_pair(uint32_t w, f16x2 s2, f16x2 b2) {
   return __builtin_elementwise_fma(q, s2, b2);
 }
 
+// The routed-step kernels' form of the same decode, the four pairs of one dword at a time.  The nibbles
+// at bits [0, 4) and [4, 8) of each half already lie inside the float16 mantissa: OR-ing the exponent
+// pattern of 1024 (0x6400) over the first gives the half 1024 + q, OR-ing that of 64 (0x5400) over the
+// second (mantissa bits [4, 8)) gives 64 + q.  So one shift by 8 serves the dword's other two pairs, and
+// each pair costs one v_and_or_b32, one exact subtraction and one packed fma.  The masks sit in scalar and
+// the patterns in vector registers: the three-operand encoding takes no literal and one scalar operand.
+struct AwqDecode {
+  uint32_t m_lo, m_hi;      // 0x000F000F, 0x00F000F0 (scalar)
+  uint32_t e1024, e64;      // 0x64006400, 0x54005400 (vector)
+};
+__device__ __forceinline__ AwqDecode awq_decode_consts() {
+  AwqDecode d;
+  asm("s_mov_b32 %0, 0xf000f" : "=s"(d.m_lo));
+  asm("s_mov_b32 %0, 0xf000f0" : "=s"(d.m_hi));
+  asm("v_mov_b32 %0, 0x64006400" : "=v"(d.e1024));
+  asm("v_mov_b32 %0, 0x54005400" : "=v"(d.e64));
+  return d;
+}
+// p[i] = the pair (local k = i, i + 4) of dword w, as awq_pair<i>.
+__device__ __forceinline__ void awq_quad(uint32_t w, f16x2 s2, f16x2 b2, const AwqDecode& d, f16x2 (&p)[4]) {
+  const uint32_t w8 = w >> 8;
+  const f16x2 c1024 = {(_Float16)-1024.0f, (_Float16)-1024.0f}, c64 = {(_Float16)-64.0f, (_Float16)-64.0f};
+  p[0] = __builtin_elementwise_fma(__builtin_bit_cast(f16x2, (w & d.m_lo) | d.e1024) + c1024, s2, b2);
+  p[1] = __builtin_elementwise_fma(__builtin_bit_cast(f16x2, (w & d.m_hi) | d.e64) + c64, s2, b2);
+  p[2] = __builtin_elementwise_fma(__builtin_bit_cast(f16x2, (w8 & d.m_lo) | d.e1024) + c1024, s2, b2);
+  p[3] = __builtin_elementwise_fma(__builtin_bit_cast(f16x2, (w8 & d.m_hi) | d.e64) + c64, s2, b2);
+}
+
 // Per-group bias RN_f16(-zero * scale), a single half multiply.
 __device__ __forceinline__ _Float16 awq_bias(uint32_t zero, _Float16 s) {
   const _Float16 nz = -(_Float16)(float)zero;

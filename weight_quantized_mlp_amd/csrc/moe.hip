@@ -17,10 +17,16 @@
 // its scale and zero.  x sits in LDS, permuted so that each dword holds the pair
 // (k, k+4) that matches the nibble extraction.  Order: per lane, groups ascending,
 // inside a group 16 dot2 steps ascending; then a butterfly over the 16 lanes.
-// Kernel 2 (W2 + ordered sum): one workgroup per 32 outputs, one wave per route reading the
-// route's 32 rows as contiguous 16-byte group pieces; per (route, output) the group partials
-// are added in group order and rounded to float16; then 32 threads sum the routes in order
-// with fmaf.
+// Kernel 2 (W2 + ordered sum): for I <= 256 one workgroup per 16 outputs (32 when I <= 64), one
+// wave per route, four (two) lanes per output row, each with a contiguous part of the row's groups;
+// per (route, output) the parts' partials are combined pairwise and rounded to float16; then the
+// workgroup's outputs sum the routes in order with fmaf.  Wider I: a workgroup per 32 outputs reading
+// the rows as contiguous 16-byte pieces, or one row per thread.
+// Decode (all kernels): each pair of nibbles becomes two float16 values with one v_and_or_b32, one
+// exact subtraction and one packed fma (three-operand forms: masks in scalar registers).
+#include <algorithm>
+#include <utility>
+
 #include "dev_common.h"
 #include "launch.h"
 
@@ -68,17 +74,18 @@ __device__ __forceinline__ void stage_pairs(uint8_t* lds, const uint16_t* __rest
 
 // Dot product of one group of 32 codes (16 bytes) with 32 LDS activations.
 __device__ __forceinline__ float awq_group_dot(const u32x4 c, _Float16 s, _Float16 b, const uint8_t* xg,
-                                               float acc) {
+                                               float acc, const AwqDecode& dc) {
   const f16x2 s2 = {s, s};
   const f16x2 b2 = {b, b};
 #pragma unroll
   for (int dw = 0; dw < 4; ++dw) {
     const u32x4 xv = *reinterpret_cast<const u32x4*>(xg + 16 * dw);
-    const uint32_t w = c[dw];
-    acc = dot2_f16(awq_pair<0>(w, s2, b2), as_f16x2(xv.x), acc);
-    acc = dot2_f16(awq_pair<1>(w, s2, b2), as_f16x2(xv.y), acc);
-    acc = dot2_f16(awq_pair<2>(w, s2, b2), as_f16x2(xv.z), acc);
-    acc = dot2_f16(awq_pair<3>(w, s2, b2), as_f16x2(xv.w), acc);
+    f16x2 p[4];
+    awq_quad(c[dw], s2, b2, dc, p);
+    acc = dot2_f16(p[0], as_f16x2(xv.x), acc);
+    acc = dot2_f16(p[1], as_f16x2(xv.y), acc);
+    acc = dot2_f16(p[2], as_f16x2(xv.z), acc);
+    acc = dot2_f16(p[3], as_f16x2(xv.w), acc);
   }
   return acc;
 }
@@ -118,6 +125,7 @@ __global__ void __launch_bounds__(256) awq_w13_kernel(int E, int H, int I, const
                                                       uint16_t* __restrict__ act,
                                                       const uint8_t* __restrict__ w2bank, int64_t w2_expert_bytes) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const AwqDecode dc = awq_decode_consts();
   const int r = blockIdx.x;
   const int nb = blockIdx.y * 8;
   const int e = ids[r];
@@ -167,7 +175,7 @@ __global__ void __launch_bounds__(256) awq_w13_kernel(int E, int H, int I, const
       if (j + 16 * i < G) {
         const _Float16 sv = f16_from_bits((uint16_t)sraw[i]);
         acc = awq_group_dot(c[i], sv, group_bias_from_raw<ML>(mraw[i], sv), lds + j * kGrpStride + 16 * i * kGrpStride,
-                            acc);
+                            acc, dc);
       }
     }
   } else {
@@ -179,7 +187,7 @@ __global__ void __launch_bounds__(256) awq_w13_kernel(int E, int H, int I, const
         const int64_t mi = (int64_t)row * G + g;
         const _Float16 s = f16_from_bits(scales[mi]);
         const _Float16 b = group_bias<ML>(expert, L, mi, s);
-        acc = awq_group_dot(c, s, b, lds + g * kGrpStride, acc);
+        acc = awq_group_dot(c, s, b, lds + g * kGrpStride, acc, dc);
       }
     }
   }
@@ -210,6 +218,7 @@ __global__ void __launch_bounds__(1024) awq_w2_kernel(int E, int topk, int H, in
                                                       const uint8_t* __restrict__ bank, AwqLayout L,
                                                       const uint16_t* __restrict__ act, uint16_t* __restrict__ out) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const AwqDecode dc = awq_decode_consts();
   const int G = I >> 5;
   const int act_bytes = G * kGrpStride;  // per route
   float* part = reinterpret_cast<float*>(lds + topk * act_bytes);  // [topk][kW2Rows][G]
@@ -248,7 +257,8 @@ __global__ void __launch_bounds__(1024) awq_w2_kernel(int E, int topk, int H, in
       const int g = pc % G;
       const _Float16 sv = f16_from_bits((uint16_t)sraw[j]);
       part[(r * kW2Rows) * G + pc] =
-          live ? awq_group_dot(c[j], sv, group_bias_from_raw<ML>(mraw[j], sv), lds + r * act_bytes + g * kGrpStride, 0.f)
+          live ? awq_group_dot(c[j], sv, group_bias_from_raw<ML>(mraw[j], sv), lds + r * act_bytes + g * kGrpStride, 0.f,
+                               dc)
                : 0.f;
     }
   }
@@ -271,84 +281,94 @@ __global__ void __launch_bounds__(1024) awq_w2_kernel(int E, int topk, int H, in
   }
 }
 
-// Kernel 2, row-pair form (G = I/32 <= 8): one workgroup per 32 outputs, one wave per route; lane l handles
-// row o0 + (l & 31) and half h = l >> 5 of its groups (h = 0: groups [0, GH), h = 1: [GH, G), GH = ceil(G/2)).
-// The lane loads its groups' codes and metadata and its route's act for those groups straight into
-// registers (act is read by all 32 lanes of a half at the same addresses), so nothing is staged in LDS
-// before the dot products.  Order per (route, row): each group's 16 dot2 steps from 0, the group partials
-// of a half added in group order, then half 0 + half 1, rounded to float16; one barrier, then 32 threads
-// add the routes in order with fmaf.
+// Kernel 2, row-part form (G = I/32 <= 8): one workgroup per RPW = 64/LPR outputs, one wave per route;
+// LPR lanes share a row: lane l handles row o0 + l % RPW and part h = l / RPW of its groups (part h:
+// groups [h GP, min((h+1) GP, G)), GP = ceil(G/LPR)).  The lane's code and metadata loads are issued
+// first; act is staged in LDS in (k, k+4) pair order (all RPW lanes of a part read the same addresses),
+// and the routes' effective weights (0 for an invalid id) go to LDS beside it, all under one barrier.
+// Order per (route, row): each group's 16 dot2 steps from 0, a part's group partials added in group order,
+// the parts combined pairwise ((p0 + p1) + (p2 + p3) ...), rounded to float16; after a second barrier RPW
+// threads add the routes in order with fmaf (an invalid route adds 0 * 0, which leaves the sum as it is).
 constexpr int kMaxRoutes = 16;   // the entry point's top-k limit (one wave per route, 1024 threads)
 
-template <int ML, int GH>
-__global__ void __launch_bounds__(1024) awq_w2_pair_kernel(int E, int topk, int H, int I,
+template <int ML, int GP>
+struct W2Lane {
+  u32x4 c[GP];
+  uint32_t sraw[GP], mraw[GP];
+};
+
+// The lane's unconditional loads from clamped addresses (an invalid id reads expert 0; groups past the
+// part's count read group G-1), so that every load of the lane is in flight before any is used.
+template <int ML, int GP>
+__device__ __forceinline__ void w2_lane_load(W2Lane<ML, GP>& t, const uint8_t* expert, const AwqLayout& L, int o,
+                                             int g0, int G, int I) {
+  const uint8_t* codes = expert + (size_t)o * (I >> 1);
+  const uint16_t* scales = reinterpret_cast<const uint16_t*>(expert + L.scale_off);
+#pragma unroll
+  for (int i = 0; i < GP; ++i) {
+    const int g = min(g0 + i, G - 1);
+    const int64_t mi = (int64_t)o * G + g;
+    t.c[i] = *reinterpret_cast<const u32x4*>(codes + 16 * g);
+    t.sraw[i] = scales[mi];
+    t.mraw[i] = group_meta2_raw<ML>(expert, L, mi);
+  }
+}
+
+// The route's value for the lane's row: group partials of the part in order, then the parts combined.
+// Every partial is computed (a clamped group from its copy) and only the part's own are added, so that
+// the uses are unconditional and the loads above stay where they are.
+template <int ML, int GP, int LPR>
+__device__ __forceinline__ float w2_lane_dot(const W2Lane<ML, GP>& t, const uint8_t* arow, int g0, int ng, int G,
+                                             const AwqDecode& dc) {
+  float acc = 0.f;
+#pragma unroll
+  for (int i = 0; i < GP; ++i) {
+    const _Float16 sv = f16_from_bits((uint16_t)t.sraw[i]);
+    const float p = awq_group_dot(t.c[i], sv, group_bias_from_raw<ML>(t.mraw[i], sv),
+                                  arow + min(g0 + i, G - 1) * kGrpStride, 0.f, dc);
+    acc = i < ng ? acc + p : acc;
+  }
+#pragma unroll
+  for (int off = 64 / LPR; off < 64; off *= 2) acc += __shfl_xor(acc, off, 64);
+  return acc;
+}
+
+template <int ML, int LPR, int GP>
+__global__ void __launch_bounds__(1024) awq_w2_part_kernel(int E, int topk, int H, int I,
                                                            const int32_t* __restrict__ ids,
                                                            const float* __restrict__ router_w,
                                                            const uint8_t* __restrict__ bank, AwqLayout L,
                                                            const uint16_t* __restrict__ act, uint16_t* __restrict__ out) {
-  __shared__ float ys[kMaxRoutes][32];
+  constexpr int RPW = 64 / LPR;
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];   // act rows, pair order
+  __shared__ float ys[kMaxRoutes][RPW];
+  __shared__ float wr[kMaxRoutes];
   const int G = I >> 5;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int r = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int row = lane & 31, h = lane >> 5;
-  const int o = blockIdx.x * 32 + row;
-  const int g0 = h * GH;
-  const int ng = h ? G - GH : GH;                     // this half's group count (0 < ng <= GH)
+  const int row = lane % RPW, h = lane / RPW;
+  const int o = blockIdx.x * RPW + row;
+  const int g0 = h * GP;
+  const int ng = min(max(G - g0, 0), GP);
   const int e = ids[r];
   const bool live = e >= 0 && e < E;
-  const uint8_t* expert = bank + (size_t)(live ? e : 0) * L.expert_bytes;
-  const uint8_t* codes = expert + (size_t)o * (I >> 1);
-  const uint16_t* scales = reinterpret_cast<const uint16_t*>(expert + L.scale_off);
-  const u32x4* ar = reinterpret_cast<const u32x4*>(act + (size_t)r * I);   // 8 halves per 16-byte chunk
-  // unconditional loads from clamped addresses (an invalid id reads expert 0; groups past this half's
-  // count read group G-1), so that every load of the lane is in flight before any is used
-  u32x4 c[GH], a[GH][4];
-  uint32_t sraw[GH], mraw[GH];
-#pragma unroll
-  for (int i = 0; i < GH; ++i) {
-    const int g = min(g0 + i, G - 1);
-    const int64_t mi = (int64_t)o * G + g;
-    c[i] = *reinterpret_cast<const u32x4*>(codes + 16 * g);
-    sraw[i] = scales[mi];
-    mraw[i] = group_meta2_raw<ML>(expert, L, mi);
+  W2Lane<ML, GP> t;
+  w2_lane_load(t, bank + (size_t)(live ? e : 0) * L.expert_bytes, L, o, g0, G, I);
+  if (tid < topk) {
+    const int er = ids[tid];
+    wr[tid] = er >= 0 && er < E ? router_w[tid] : 0.f;
   }
-#pragma unroll
-  for (int i = 0; i < GH; ++i)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) a[i][q] = ar[4 * min(g0 + i, G - 1) + q];
-  // every group's partial is computed (a group past this half's count from its clamped copy) and only the
-  // valid ones are added, in group order: with the uses unconditional the loads above stay where they are
-  // (a conditional use lets the compiler sink its loads into the condition, one round trip each)
-  float acc = 0.f;
-#pragma unroll
-  for (int i = 0; i < GH; ++i) {
-    const _Float16 sv = f16_from_bits((uint16_t)sraw[i]), bv = group_bias_from_raw<ML>(mraw[i], sv);
-    const f16x2 s2 = {sv, sv}, b2 = {bv, bv};
-    float p = 0.f;
-#pragma unroll
-    for (int dw = 0; dw < 4; ++dw) {
-      const u32x4 v = a[i][dw];               // k = 8 dw .. 8 dw + 7 of the group, natural order
-      const uint32_t x04 = (v.x & 0xffffu) | (v.z << 16), x15 = (v.x >> 16) | (v.z & 0xffff0000u);
-      const uint32_t x26 = (v.y & 0xffffu) | (v.w << 16), x37 = (v.y >> 16) | (v.w & 0xffff0000u);
-      const uint32_t w = c[i][dw];
-      p = dot2_f16(awq_pair<0>(w, s2, b2), as_f16x2(x04), p);
-      p = dot2_f16(awq_pair<1>(w, s2, b2), as_f16x2(x15), p);
-      p = dot2_f16(awq_pair<2>(w, s2, b2), as_f16x2(x26), p);
-      p = dot2_f16(awq_pair<3>(w, s2, b2), as_f16x2(x37), p);
-    }
-    acc = i < ng ? acc + p : acc;
-  }
-  const float other = __shfl_xor(acc, 32, 64);      // the row's other half
-  if (h == 0 && r < topk) ys[r][row] = live ? (float)(_Float16)(acc + other) : 0.f;   // per-route float16
+  stage_pairs(lds, act, I, topk, G * kGrpStride);
   __syncthreads();
-  if (tid < 32) {
+  const AwqDecode dc = awq_decode_consts();
+  const float y = w2_lane_dot<ML, GP, LPR>(t, lds + r * G * kGrpStride, g0, ng, G, dc);
+  if (h == 0) ys[r][row] = live ? (float)(_Float16)y : 0.f;   // per-route float16
+  __syncthreads();
+  if (tid < RPW) {
     float sum = 0.f;
-    for (int rr = 0; rr < topk; ++rr) {
-      const int er = ids[rr];
-      if (er >= 0 && er < E) sum = fmaf(router_w[rr], ys[rr][tid], sum);
-    }
-    out[blockIdx.x * 32 + tid] = __builtin_bit_cast(uint16_t, (_Float16)sum);
+    for (int rr = 0; rr < topk; ++rr) sum = fmaf(wr[rr], ys[rr][tid], sum);
+    out[blockIdx.x * RPW + tid] = __builtin_bit_cast(uint16_t, (_Float16)sum);
   }
 }
 
@@ -361,6 +381,7 @@ __global__ void __launch_bounds__(512) awq_w2_rows_kernel(int E, int topk, int H
                                                      const uint8_t* __restrict__ bank, AwqLayout L,
                                                      const uint16_t* __restrict__ act, uint16_t* __restrict__ out) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const AwqDecode dc = awq_decode_consts();
   const int G = I >> 5;
   const int act_bytes = G * kGrpStride;  // per route
   float* ys = reinterpret_cast<float*>(lds + topk * act_bytes);  // [topk][32]
@@ -383,7 +404,7 @@ __global__ void __launch_bounds__(512) awq_w2_rows_kernel(int E, int topk, int H
         const int64_t mi = (int64_t)o * G + g;
         const _Float16 s = f16_from_bits(scales[mi]);
         const _Float16 b = group_bias<ML>(expert, L, mi, s);
-        acc = awq_group_dot(c, s, b, lds + r * act_bytes + g * kGrpStride, acc);
+        acc = awq_group_dot(c, s, b, lds + r * act_bytes + g * kGrpStride, acc, dc);
       }
       v = (float)(_Float16)acc;  // per-route float16 materialisation
     }
@@ -398,6 +419,37 @@ __global__ void __launch_bounds__(512) awq_w2_rows_kernel(int E, int topk, int H
     }
     out[o] = __builtin_bit_cast(uint16_t, (_Float16)acc);
   }
+}
+
+// W2 row-part form for G groups per row: lanes per row and groups per lane part.  Two lanes per row for
+// G <= 2, else kW2Lanes (more, smaller workgroups spread the step's dot products over more CUs).
+constexpr int kW2Lanes = 4;
+struct W2Form {
+  int lpr, gp;
+};
+W2Form w2_form(int G) {
+  if (G <= 2) return {2, 1};
+  return {kW2Lanes, (G + kW2Lanes - 1) / kW2Lanes};
+}
+
+// Calls f(integral_constant<int, v>) for the v in Is... equal to x.
+template <typename F, int... Is>
+void dispatch_int(int x, F&& f, std::integer_sequence<int, Is...>) {
+  (void)((x == Is ? (f(std::integral_constant<int, Is>{}), true) : false) || ...);
+}
+
+// f(ml, lpr, gp) with compile-time metadata layout, lanes per row and groups per part.
+template <typename F>
+void dispatch_w2(int meta_layout, W2Form form, F&& f) {
+  auto with_ml = [&](auto ml) {
+    auto with_gp = [&](auto lpr) {
+      dispatch_int(form.gp, [&](auto gp) { f(ml, lpr, gp); }, std::integer_sequence<int, 1, 2, 3, 4>{});
+    };
+    if (form.lpr == 2) with_gp(std::integral_constant<int, 2>{});
+    else with_gp(std::integral_constant<int, kW2Lanes>{});
+  };
+  if (meta_layout == 3) with_ml(std::integral_constant<int, 3>{});
+  else with_ml(std::integral_constant<int, 4>{});
 }
 
 }  // namespace
@@ -436,26 +488,16 @@ hipError_t launch_moe_awq_m1(int E, int topk, int H, int I, const uint16_t* x, c
   if (err != hipSuccess) return err;
   const size_t lds2 = (size_t)topk * (I / 32) * kGrpStride + (size_t)topk * kW2Rows * (I / 32 + 1) * 4;
   const int ppl2 = (kW2Rows * (I / 32) + 63) / 64;  // 16-byte pieces per lane in W2
-  const int gh = (I / 32 + 1) / 2;                  // groups per half row in the row-pair form
-  if (gh <= 4) {
-    const dim3 g2(H / 32);
-#define WQ_W2P(ML, GH)                                                                                           \
-  hipLaunchKernelGGL((awq_w2_pair_kernel<ML, GH>), g2, dim3(64 * topk), 0, st, E, topk, H, I, ids, router_w, w2, L2, \
-                     act, out)
-#define WQ_W2P_ML(ML)              \
-  switch (gh) {                    \
-    case 1: WQ_W2P(ML, 1); break;  \
-    case 2: WQ_W2P(ML, 2); break;  \
-    case 3: WQ_W2P(ML, 3); break;  \
-    default: WQ_W2P(ML, 4); break; \
-  }
-    if (meta_layout == 3) {
-      WQ_W2P_ML(3)
-    } else {
-      WQ_W2P_ML(4)
-    }
-#undef WQ_W2P_ML
-#undef WQ_W2P
+  const int G2 = I / 32;                            // groups per W2 row
+  if (G2 <= 8) {
+    const W2Form f = w2_form(G2);
+    const size_t ldsp = (size_t)topk * G2 * kGrpStride;
+    const dim3 g2(H / (64 / f.lpr));
+    auto go = [&](auto ml, auto lpr, auto gp) {
+      hipLaunchKernelGGL((awq_w2_part_kernel<decltype(ml)::value, decltype(lpr)::value, decltype(gp)::value>), g2,
+                         dim3(64 * topk), ldsp, st, E, topk, H, I, ids, router_w, w2, L2, act, out);
+    };
+    dispatch_w2(meta_layout, f, go);
   } else if (ppl2 <= 8 && lds2 <= 65536) {
     const dim3 g2((H + kW2Rows - 1) / kW2Rows);
 #define WQ_W2(ML, P)                                                                                          \
