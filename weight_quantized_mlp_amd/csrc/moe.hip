@@ -11,12 +11,13 @@
 // The step moves ~7 MB, about 28 KB per CU, so it is bound by memory latency: both kernels
 // issue all of a lane's weight loads at once (compile-time group count per lane) before
 // staging the activations, so weights and activations arrive in one round trip.
-// Kernel 1 (W13 + SwiGLU): one workgroup per (route, 8 consecutive n).  A wave holds
-// four 16-lane row groups: (gate n, up n, gate n+1, up n+1); lane j of a group owns
-// the groups of 32 k  g = j, j+16, ...: one coalesced 16-byte code load per group plus
-// its scale and zero.  x sits in LDS, permuted so that each dword holds the pair
-// (k, k+4) that matches the nibble extraction.  Order: per lane, groups ascending,
-// inside a group 16 dot2 steps ascending; then a butterfly over the 16 lanes.
+// Kernel 1 (W13 + SwiGLU): one workgroup per (route, 4 consecutive n), a wave per n holding two
+// 32-lane row groups (gate n, up n); for H < 1536 one per (route, 8 n) with four 16-lane row groups
+// (gate n, up n, gate n+1, up n+1).  Lane j of a group owns the groups of 32 k  g = j, j+RL, ...: one
+// coalesced 16-byte code load per group plus its scale and zero.  x sits in LDS, permuted so that each
+// dword holds the pair (k, k+4) that matches the nibble extraction.  Order: per lane, groups ascending,
+// inside a group 16 dot2 steps ascending; then the 16-lane rows summed by DPP (lane^1, lane^2, half-row
+// and row mirrors) and, for 32-lane groups, the two rows added.
 // Kernel 2 (W2 + ordered sum): for I <= 256 one workgroup per 16 outputs (32 when I <= 64), one
 // wave per route, four (two) lanes per output row, each with a contiguous part of the row's groups;
 // per (route, output) the parts' partials are combined pairwise and rounded to float16; then the
@@ -115,10 +116,11 @@ __device__ __forceinline__ _Float16 group_bias_from_raw(uint32_t raw, _Float16 s
 // gridDim.y-th) of its route's W2 expert block, so that the W2 kernel finds those bytes in the
 // memory-side cache instead of waiting a DRAM round trip.  The values only feed an empty asm at the end
 // (kept live, never stored).  kPrefetchPerThread 16-byte loads per thread cover a 20-workgroup route of a
-// 243 KB W2 expert (3-byte metadata) and most of a 4-byte one.
+// 243 KB W2 expert (3-byte metadata) and most of a 4-byte one; loads past a workgroup's share repeat its
+// last unit.
 constexpr int kPrefetchPerThread = 3;   // (the end-of-kernel asm below names three)
 
-template <int ML, int GPL>
+template <int ML, int GPL, int RL>
 __global__ void __launch_bounds__(256) awq_w13_kernel(int E, int H, int I, const uint16_t* __restrict__ x,
                                                       const int32_t* __restrict__ ids,
                                                       const uint8_t* __restrict__ bank, AwqLayout L,
@@ -126,18 +128,19 @@ __global__ void __launch_bounds__(256) awq_w13_kernel(int E, int H, int I, const
                                                       const uint8_t* __restrict__ w2bank, int64_t w2_expert_bytes) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const AwqDecode dc = awq_decode_consts();
+  constexpr int NPW = 32 / RL;                         // n per wave: RL lanes per row, a gate and an up row each
   const int r = blockIdx.x;
-  const int nb = blockIdx.y * 8;
+  const int nb = blockIdx.y * 4 * NPW;
   const int e = ids[r];
   const int tid = threadIdx.x;
   if (e < 0 || e >= E) {  // invalid id: zero act row, no contribution
-    if (tid < 8 && nb + tid < I) act[(size_t)r * I + nb + tid] = 0;
+    if (tid < 4 * NPW && nb + tid < I) act[(size_t)r * I + nb + tid] = 0;
     return;
   }
   const int lane = tid & 63;
-  const int j = lane & 15;
-  const int rg = lane >> 4;
-  const int n = nb + 2 * (tid >> 6) + (rg >> 1);
+  const int j = lane & (RL - 1);
+  const int rg = lane / RL;
+  const int n = nb + NPW * (tid >> 6) + (rg >> 1);
   const int row = (rg & 1) ? n + I : n;
   const int G = H >> 5;
   const uint8_t* expert = bank + (size_t)e * L.expert_bytes;
@@ -159,7 +162,7 @@ __global__ void __launch_bounds__(256) awq_w13_kernel(int E, int H, int I, const
     uint32_t sraw[GPL], mraw[GPL];
 #pragma unroll
     for (int i = 0; i < GPL; ++i) {
-      const int g = min(j + 16 * i, G - 1);
+      const int g = min(j + RL * i, G - 1);
       const int64_t mi = (int64_t)row * G + g;
       c[i] = *reinterpret_cast<const u32x4*>(codes + 16 * g);
       sraw[i] = scales[mi];
@@ -167,22 +170,22 @@ __global__ void __launch_bounds__(256) awq_w13_kernel(int E, int H, int I, const
     }
 #pragma unroll
     for (int i = 0; i < kPrefetchPerThread; ++i)
-      pf[i] = w2e[min(u0 + tid + 256 * i, (int64_t)w2_units - 1)];   // past the share: repeats a byte range
+      pf[i] = w2e[min(u0 + tid + 256 * i, min(u0 + per_wg, w2_units) - 1)];
     stage_pairs(lds, x, H, 1, 0);
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < GPL; ++i) {
-      if (j + 16 * i < G) {
+      if (j + RL * i < G) {
         const _Float16 sv = f16_from_bits((uint16_t)sraw[i]);
-        acc = awq_group_dot(c[i], sv, group_bias_from_raw<ML>(mraw[i], sv), lds + j * kGrpStride + 16 * i * kGrpStride,
-                            acc, dc);
+        acc = awq_group_dot(c[i], sv, group_bias_from_raw<ML>(mraw[i], sv), lds + (j + RL * i) * kGrpStride, acc,
+                            dc);
       }
     }
   } else {
     stage_pairs(lds, x, H, 1, 0);
     __syncthreads();
     if (n < I) {
-      for (int g = j; g < G; g += 16) {
+      for (int g = j; g < G; g += RL) {
         const u32x4 c = *reinterpret_cast<const u32x4*>(codes + 16 * g);
         const int64_t mi = (int64_t)row * G + g;
         const _Float16 s = f16_from_bits(scales[mi]);
@@ -191,8 +194,9 @@ __global__ void __launch_bounds__(256) awq_w13_kernel(int E, int H, int I, const
       }
     }
   }
-  acc = group_sum<16>(acc);
-  const float u = __shfl_down(acc, 16, 64);
+  acc = row16_sum(acc);                                // the row's lanes: DPP within 16 lanes ...
+  if constexpr (RL == 32) acc += __shfl_xor(acc, 16, 64);   // ... then the two halves
+  const float u = __shfl_down(acc, RL, 64);
   if (j == 0 && (rg & 1) == 0 && n < I) {
     const float gh = (float)(_Float16)acc;
     const float uh = (float)(_Float16)u;
@@ -460,11 +464,17 @@ hipError_t launch_moe_awq_m1(int E, int topk, int H, int I, const uint16_t* x, c
   const AwqLayout L13 = awq_layout(2 * (int64_t)I, H, meta_layout);
   const AwqLayout L2 = awq_layout(H, I, meta_layout);
   const size_t lds13 = (size_t)(H / 32) * kGrpStride;
-  const dim3 g13(topk, (I + 7) / 8);
-  const int gpl13 = (H / 32 + 15) / 16;  // groups per lane in W13
-#define WQ_W13(ML, P)                                                                                     \
-  hipLaunchKernelGGL((awq_w13_kernel<ML, P>), g13, dim3(256), lds13, st, E, H, I, x, ids, w13, L13, act, w2, \
-                     L2.expert_bytes)
+  // 32 lanes per row (4 n per workgroup) once a 16-lane row would hold 3 or more groups per lane
+  const int rl = (H / 32 + 15) / 16 >= 3 ? 32 : 16;
+  const dim3 g13(topk, (I + 128 / rl - 1) / (128 / rl));
+  const int gpl13 = (H / 32 + rl - 1) / rl;  // groups per lane in W13
+#define WQ_W13(ML, P)                                                                                          \
+  if (rl == 32)                                                                                                \
+    hipLaunchKernelGGL((awq_w13_kernel<ML, P, 32>), g13, dim3(256), lds13, st, E, H, I, x, ids, w13, L13, act, \
+                       w2, L2.expert_bytes);                                                                   \
+  else                                                                                                         \
+    hipLaunchKernelGGL((awq_w13_kernel<ML, P, 16>), g13, dim3(256), lds13, st, E, H, I, x, ids, w13, L13, act, \
+                       w2, L2.expert_bytes)
 #define WQ_W13_ML(ML)                                                                     \
   switch (gpl13) {                                                                        \
     case 1: WQ_W13(ML, 1); break;                                                         \
