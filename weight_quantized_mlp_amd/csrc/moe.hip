@@ -445,12 +445,14 @@ void dispatch_int(int x, F&& f, std::integer_sequence<int, Is...>) {
 // f(ml, lpr, gp) with compile-time metadata layout, lanes per row and groups per part.
 template <typename F>
 void dispatch_w2(int meta_layout, W2Form form, F&& f) {
+  static_assert(kW2Lanes == 4, "the part counts below assume four lanes per row (G <= 8: one or two groups)");
   auto with_ml = [&](auto ml) {
-    auto with_gp = [&](auto lpr) {
-      dispatch_int(form.gp, [&](auto gp) { f(ml, lpr, gp); }, std::integer_sequence<int, 1, 2, 3, 4>{});
-    };
-    if (form.lpr == 2) with_gp(std::integral_constant<int, 2>{});
-    else with_gp(std::integral_constant<int, kW2Lanes>{});
+    if (form.lpr == 2) {
+      f(ml, std::integral_constant<int, 2>{}, std::integral_constant<int, 1>{});
+    } else {
+      dispatch_int(form.gp, [&](auto gp) { f(ml, std::integral_constant<int, kW2Lanes>{}, gp); },
+                   std::integer_sequence<int, 1, 2>{});
+    }
   };
   if (meta_layout == 3) with_ml(std::integral_constant<int, 3>{});
   else with_ml(std::integral_constant<int, 4>{});
