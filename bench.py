@@ -64,7 +64,8 @@ def parse():
     ap.add_argument("--counters", type=int, default=0,
                     help="only run this many plain (non-graph) headline steps, for rocprofv3 --pmc passes")
     ap.add_argument("--prefill-counters", type=int, default=0,
-                    help="only run this many plain NVFP4 M=512 prefill steps, for rocprofv3 --pmc passes")
+                    help="only run this many plain NVFP4 prefill steps (M from --prefill-m), for rocprofv3 passes")
+    ap.add_argument("--prefill-m", type=int, default=512, help="rows of the --prefill-counters steps (512 or 8192)")
     ap.add_argument("--decode-counters", type=int, default=0,
                     help="only run this many plain NVFP4 M=1 decode steps (8 rotating weight copies), for rocprofv3")
     ap.add_argument("--fp8-prefill-counters", type=int, default=0,
@@ -535,7 +536,7 @@ def counter_modes(args, torch, wq, synth, dev):
         return True
     if args.prefill_counters or args.decode_counters:
         blk, gs = nvfp4_weights(torch, wq, synth.nvfp4_mlp_weights(), dev)
-        M, copies, n = (512, 1, args.prefill_counters) if args.prefill_counters else (1, 8, args.decode_counters)
+        M, copies, n = (args.prefill_m, 1, args.prefill_counters) if args.prefill_counters else (1, 8, args.decode_counters)
         sets = [blk] + [{k: t.clone() for k, t in blk.items()} for _ in range(copies - 1)]
         xb, _ = synth.nvfp4_x(M, outlier_frac=0.01 if M > 1 else 0.0)
         x = torch.from_numpy(xb.view("int16")).to(dev).view(torch.bfloat16)
