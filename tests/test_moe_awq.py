@@ -141,9 +141,10 @@ def test_rotating_ids_and_determinism(moe):
 # Shapes reaching every kernel form of the step: the W2 row-part kernel with two lanes per row (I = 32,
 # 64) and four lanes per row with one or two groups per lane (I = 96, 128 / 192, 256), the piece kernel
 # (I = 320, 512) and the per-row kernel (I = 1024); W13 with 1..8 groups per lane (H = 256 .. 4096) and
-# its runtime loop (H = 8192); top-k 1, 3, 16.
+# its runtime loop (H = 8192); top-k 1, 3, 16 (16 routes: 1024-thread workgroups in both W2 forms).
 MOE_SHAPES = [(24, 3, 256, 32), (24, 16, 512, 64), (24, 1, 256, 96), (40, 10, 2048, 128), (24, 5, 768, 192),
-              (24, 4, 512, 256), (24, 3, 256, 320), (20, 2, 512, 512), (12, 2, 256, 1024), (12, 3, 8192, 64)]
+              (24, 4, 512, 256), (24, 16, 256, 192), (24, 3, 256, 320), (20, 2, 512, 512), (12, 2, 256, 1024),
+              (12, 3, 8192, 64)]
 
 
 @pytest.mark.parametrize("E,topk,Hs,Is", MOE_SHAPES)
@@ -166,3 +167,31 @@ def test_moe_shapes(E, topk, Hs, Is, ml):
     assert ulp_dist(out, pair_out).max() <= 4
     if topk >= 3:
         assert np.all(act[1] == 0) and np.array_equal(act[0], act[2])
+
+
+def test_graph_replays_match_eager(moe):
+    """The step captured once and replayed with new ids copied in between (as a serving loop would):
+    every replay equals the eager call on the same ids, bit for bit."""
+    d, banks = moe
+    E = d["w13"][0].shape[0]
+    x = f16_dev(d["x_bits"])
+    rw = dev(np.asarray(d["router_w"], dtype=np.float32))
+    ids = dev(np.asarray(d["ids"], dtype=np.int32))
+    act = torch.empty((len(d["ids"]), I), dtype=torch.float16, device=DEV)
+    out = torch.empty((H,), dtype=torch.float16, device=DEV)
+    wq.moe_awq_m1_run(x, ids, rw, *banks[3], E, I, 3, act=act, out=out)     # warm-up outside capture
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            wq.moe_awq_m1_run(x, ids, rw, *banks[3], E, I, 3, act=act, out=out)
+    torch.cuda.synchronize()
+    for rep, r in enumerate(synth.awq_rotating_ids(4, len(d["ids"]), E)):
+        ids.copy_(torch.from_numpy(np.asarray(r, dtype=np.int32)).to(DEV))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        o_graph, a_graph = host(out).view(np.uint16).copy(), host(act).view(np.uint16).copy()
+        o_eager, a_eager = run(d, banks, r)
+        assert np.array_equal(o_graph, o_eager) and np.array_equal(a_graph, a_eager), rep
