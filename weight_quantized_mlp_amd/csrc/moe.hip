@@ -12,7 +12,7 @@
 // issue all of a lane's weight loads at once (compile-time group count per lane) before
 // staging the activations, so weights and activations arrive in one round trip.
 // Kernel 1 (W13 + SwiGLU): one workgroup per (route, 4 consecutive n), a wave per n holding two
-// 32-lane row groups (gate n, up n); for H < 1536 one per (route, 8 n) with four 16-lane row groups
+// 32-lane row groups (gate n, up n); for H < 1056 one per (route, 8 n) with four 16-lane row groups
 // (gate n, up n, gate n+1, up n+1).  Lane j of a group owns the groups of 32 k  g = j, j+RL, ...: one
 // coalesced 16-byte code load per group plus its scale and zero.  x sits in LDS, permuted so that each
 // dword holds the pair (k, k+4) that matches the nibble extraction.  Order: per lane, groups ascending,
