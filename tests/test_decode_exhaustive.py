@@ -93,7 +93,10 @@ def check_columns(y, dq, ks, what):
 
 
 # ---- single linear ---------------------------------------------------------------------------------------
-FP8_LINEAR = [(p, x, K) for p in ("gemv", "mfma") for x in ("f32", "bf16") for K in (64, 192, 512)]
+# K = 4096 (a million weights at N = 256) reaches the GEMV item kernel (fp8_lin_items); the smaller K the
+# general GEMV kernel (fp8w_gemv_kernel)
+FP8_LINEAR = ([(p, x, K) for p in ("gemv", "mfma") for x in ("f32", "bf16") for K in (64, 192, 512)]
+              + [("gemv", x, 4096) for x in ("f32", "bf16")])
 
 
 @pytest.mark.parametrize("path,xdt,K", FP8_LINEAR)
