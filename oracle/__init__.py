@@ -22,9 +22,9 @@ cites the page and section it follows:
   8-bit activation quantization of the W4A8 variant (actquant.py).
 
 Pins (what ties each function to something other than itself) are in
-``tests/test_oracle.py``.  Parity unpinned: the full-size MLP results at the
-27B tail-layer shape have no printed values on the pages; they are pinned only
-through the definitions (the same functions are pinned at small sizes).
+``tests/test_oracle.py``.  The pages print no values for the full-size MLP at
+the 27B tail-layer shape; there the oracle's act and out are checked on sampled
+rows against pure-Python sums over independently decoded weights.
 """
 from .codecs import e4m3_to_f64, e2m1_to_f64, bf16_bits_to_f64, f16_bits_to_f64
 from .dequant import (fp8w_dequant, nvfp4_dequant, nvfp4_dequant_parts, awq_dequant, awq_dequant_parts,

@@ -294,6 +294,82 @@ def test_nvfp4_mlp_matches_bruteforce_small():
     assert scale > 1e-3 and err < 1e-12
 
 
+# ---- the MLP at the decode workloads' full size (hidden 5120, intermediate 17408), sampled -------------
+# The oracle's full-size act and out against pure-Python sums with weights decoded by other means (torch's
+# float8 cast; the E2M1 table times that cast for NVFP4): act on sampled intermediate rows from x, out on
+# sampled output rows from the oracle's own act (pinned by the first check).  Indices include both ends.
+FULL_I_SAMPLES = [0, 1, 4095, 8704, 13001, 17406, 17407]
+FULL_O_SAMPLES = [0, 1, 2047, 2560, 4099, 5119]
+
+
+def _py_dot(a, b):
+    acc = 0.0
+    for u, v in zip(a, b):
+        acc += u * v
+    return acc
+
+
+def _py_silu(z):
+    return z / (1.0 + math.exp(-z)) if z >= 0 else z * math.exp(z) / (1.0 + math.exp(z))
+
+
+def _check_full_size(x, act, out, dq_gate_row, dq_up_row, dq_down_row):
+    xs = [float(v) for v in x]
+    got, want = [], []
+    for i in FULL_I_SAMPLES:
+        g = _py_dot(xs, dq_gate_row(i))
+        u = _py_dot(xs, dq_up_row(i))
+        got.append(act[i])
+        want.append(_py_silu(g) * u)
+    err, scale = oracle.normwise_rel_err(np.array(got), np.array(want))
+    assert scale > 1e-6 and err < 1e-12, err
+    acts = [float(v) for v in act]
+    got, want = [], []
+    for o in FULL_O_SAMPLES:
+        got.append(out[o])
+        want.append(_py_dot(acts, dq_down_row(o)))
+    err, scale = oracle.normwise_rel_err(np.array(got), np.array(want))
+    assert scale > 1e-6 and err < 1e-12, err
+
+
+def test_fp8_mlp_full_size_sampled():
+    d = synth.fp8_mlp(M=1)
+    x = codecs.bf16_bits_to_f64(d["x_bits"])
+    out, act = mlp.mlp_fp8w_ref(x, d["w_gate"], d["s_gate"], d["w_up"], d["s_up"], d["w_down"], d["s_down"],
+                                return_act=True)
+
+    def row(w, sc):
+        return lambda n: [float(v) * float(sc[n]) for v in torch_e4m3(w[n])]
+
+    _check_full_size(x[0], act[0], out[0], row(d["w_gate"], d["s_gate"]), row(d["w_up"], d["s_up"]),
+                     row(d["w_down"], d["s_down"]))
+
+
+def test_nvfp4_mlp_full_size_sampled():
+    w = synth.nvfp4_mlp_weights()
+    xb, _ = synth.nvfp4_x(1)
+    x = codecs.bf16_bits_to_f64(xb)
+    blk = {n: pack.block64_pack(w["wp_" + n], w["ws_" + n]) for n in ("gate", "up", "down")}
+    out, act = mlp.mlp_nvfp4_ref(x, blk["gate"], w["gs_gate"], blk["up"], w["gs_up"], blk["down"], w["gs_down"],
+                                 return_act=True)
+    table = OCP_E2M1 + [-v for v in OCP_E2M1]
+
+    def row(n):   # from the checkpoint tensors, not the Block64 records
+        wp, ws = w["wp_" + n], w["ws_" + n]
+        inv = float(np.float32(1.0) / np.float32(w["gs_" + n]))
+
+        def f(r):
+            d = torch_e4m3(ws[r])
+            vals = []
+            for j, byte in enumerate(wp[r].tolist()):
+                for nib in (byte & 15, byte >> 4):
+                    vals.append(table[nib] * float(d[(2 * j) // 16]) * inv)
+            return vals
+        return f
+
+    _check_full_size(x[0], act[0], out[0], row("gate"), row("up"), row("down"))
+
+
 def test_mlp_invariants():
     d = synth.fp8_tiny(2)
     args = (d["w_gate"], d["s_gate"], d["w_up"], d["s_up"], d["w_down"], d["s_down"])
