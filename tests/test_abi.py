@@ -304,3 +304,23 @@ def test_read_probe_validation(L):
     assert L.wq_read_probe(A, 1 << 20, A + (1 << 30), 0, None) == EINVAL
     assert L.wq_read_probe(A + 8, 1 << 20, A + (1 << 30), 8, None) == EALIGN
     assert L.wq_read_probe(A, 1 << 20, A + 4096, 8, None) == EOVERLAP
+
+
+def test_c_consumer_compiles_links_and_runs(L, tmp_path):
+    # the header as strict C99 and the library linked by a C program (tests/c_consumer.c)
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no C compiler")
+    if os.environ.get("WQMLP_LIBRARY"):
+        pytest.skip("another build of the library is loaded (the sanitizer build needs its runtime linked)")
+    libdir = os.path.dirname(os.path.abspath(wq.lib_path))
+    exe = str(tmp_path / "c_consumer")
+    r = subprocess.run([gcc, "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror",
+                        "-I", os.path.join(ROOT, "include"), os.path.join(ROOT, "tests", "c_consumer.c"),
+                        "-L", libdir, "-l:" + os.path.basename(wq.lib_path), "-Wl,-rpath," + libdir, "-o", exe],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0 and r.stdout.strip() == "c consumer ok", (r.returncode, r.stdout, r.stderr)
