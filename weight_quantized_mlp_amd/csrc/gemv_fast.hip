@@ -189,8 +189,12 @@ __global__ void __launch_bounds__(64 * kRowWaves) fp8_gu_row(int M, int K, int N
 
 // ---- NVFP4 gate+up row kernel (bf16 x), group mapping ---------------------------------------------
 // Unit of work per lane: one 16-weight group = 8 nibble bytes (qs[8q..8q+7] of its record) plus the
-// record's scale byte d[q].  Lane l owns groups l, l+64, ... of its row; the four lanes 4j..4j+3 read
-// record j's 32 nibble bytes contiguously, so a wave's loads cover the row's records without gaps.
+// record's scale byte d[q].  Lane l owns groups l, l+64, ... of its row; lane 4j+q reads bytes
+// [8q, 8q+12) of record j, i.e. the dword before its nibbles and the nibbles, so the quad's loads cover
+// the record once and a wave's loads cover 16 records without gaps or overlap.  The dword before the
+// nibbles of group 0 is the record's scale dword, which lane 4j passes to its quad (a DPP quad
+// broadcast).  The loads carry the non-temporal hint: every byte is read by exactly one load (with
+// separate loads for the nibbles and the scale byte the hint cost 4 us: the two loads share lines).
 // Workgroup shape and x staging as in the FP8 row kernel.
 // O16: act is stored as float16 bits (the NVFP4 MLP's act), else float32.
 template <int CH, bool ONE, bool O16>
@@ -208,16 +212,14 @@ __global__ void __launch_bounds__(64 * kRowWaves) nv_gu_grp(int M, int K, int N,
   // the workgroup barrier then waits only for x, not for every wave's weights.
   StageRegs<uint16_t, kRowStageRegs> sr;
   if constexpr (ONE) sr.issue(x, G);
-  u32x2 q[2][CH];
-  uint32_t sc[2][CH];
+  u32x3 wv[2][CH];   // record bytes [8q, 8q+12): .x the scale dword (q = 0), .y .z the group's nibbles
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
     const int g = min(lane + 64 * c, G - 1);   // clamped: in bounds, never accumulated
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
-      const uint8_t* p = (mt ? bu : bg) + (size_t)rl * rb + (size_t)(g >> 2) * 36;
-      q[mt][c] = ld8a4(p + 4 + 8 * (g & 3));
-      sc[mt][c] = p[g & 3];
+      const uint8_t* p = (mt ? bu : bg) + (size_t)rl * rb + (size_t)(g >> 2) * 36 + 8 * (g & 3);
+      wv[mt][c] = __builtin_nontemporal_load(reinterpret_cast<const u32x3*>(__builtin_assume_aligned(p, 8)));
     }
   }
   const int Mloop = ONE ? 1 : M;
@@ -233,12 +235,19 @@ __global__ void __launch_bounds__(64 * kRowWaves) nv_gu_grp(int M, int K, int N,
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       const int g = lane + 64 * c;
+      // the record's scale dword from the quad's first lane (G is a multiple of 4, so quads never straddle
+      // the clamped tail), then this group's byte d[q]
+      uint32_t sq[2];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+        sq[mt] = ((uint32_t)__builtin_amdgcn_mov_dpp((int)wv[mt][c].x, 0x00, 0xf, 0xf, false) >> (8 * (lane & 3))) &
+                 0xffu;
       if (g < G) {
         const u32x4 x0 = *reinterpret_cast<const u32x4*>(lds + (size_t)g * 16);
         const u32x4 x1 = *reinterpret_cast<const u32x4*>(lds + ((size_t)G + g) * 16);
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
-          const u32x2 w = q[mt][c];
+          const u32x2 w = {wv[mt][c].y, wv[mt][c].z};
           float pt = 0.f;
           pt = dot2_bf16(e2m1x2_bf16<0>(w.x), x0.x, pt);
           pt = dot2_bf16(e2m1x2_bf16<1>(w.x), x0.y, pt);
@@ -248,7 +257,7 @@ __global__ void __launch_bounds__(64 * kRowWaves) nv_gu_grp(int M, int K, int N,
           pt = dot2_bf16(e2m1x2_bf16<1>(w.y), x1.y, pt);
           pt = dot2_bf16(e2m1x2_bf16<2>(w.y), x1.z, pt);
           pt = dot2_bf16(e2m1x2_bf16<3>(w.y), x1.w, pt);
-          acc[mt] = fmaf(pt, e4m3_byte_f32<0>(sc[mt][c]), acc[mt]);
+          acc[mt] = fmaf(pt, e4m3_byte_f32<0>(sq[mt]), acc[mt]);
         }
       }
     }
@@ -581,7 +590,8 @@ __global__ void __launch_bounds__(64 * kItemWaves, 8) nv_lin_grp(int M, int K, i
 // matrix.  Work item (row i, slot t) = the 32 records [32 t, 32 t + 32) of the row, 1152 contiguous
 // bytes; items are dealt round-robin to the waves.  Both the activation rows and the items move by
 // global->LDS copies (kR32Depth items in flight per wave, explicit vmcnt waits): register loads of
-// the same data made the compiler wait for every outstanding load at the top of the item loop.
+// the same data made the compiler wait for every outstanding load at the top of the item loop.  The item
+// copies carry the non-temporal hint (each weight byte is copied once).
 // MR activation rows share one pass over the weights (each item is decoded once and used for all MR
 // rows); a call with more rows makes ceil(M / MR) passes.
 // Lane l of an item owns groups 2l, 2l+1 (record l / 2, 16 nibble bytes and 2 scale bytes).
@@ -671,8 +681,8 @@ __global__ void __launch_bounds__(64 * kItemWaves) nv_lin_r32(int M, int K, int 
       const uint32_t st = ring + stage * kR32Item;
       const uint8_t* rowp = blk + (size_t)min(rowof(lg), N - 1) * rb;   // 64-bit row base, 32-bit offsets in the row
       const uint32_t off = 1152u * lt;
-      lds_copy16(min(off + q0, rb - 16u), rowp, __builtin_amdgcn_readfirstlane(st));
-      if (lane < 8) lds_copy16(min(off + q1, rb - 16u), rowp, __builtin_amdgcn_readfirstlane(st + 1024));
+      lds_copy16_nt(min(off + q0, rb - 16u), rowp, __builtin_amdgcn_readfirstlane(st));
+      if (lane < 8) lds_copy16_nt(min(off + q1, rb - 16u), rowp, __builtin_amdgcn_readfirstlane(st + 1024));
       ++lk;
       if (lk < nk) {                                   // past the wave's last item: repeat it (never used)
         lt += NW;
