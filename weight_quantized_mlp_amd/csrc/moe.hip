@@ -164,7 +164,10 @@ __global__ void __launch_bounds__(256) awq_w13_kernel(int E, int H, int I, const
     for (int i = 0; i < GPL; ++i) {
       const int g = min(j + RL * i, G - 1);
       const int64_t mi = (int64_t)row * G + g;
-      c[i] = *reinterpret_cast<const u32x4*>(codes + 16 * g);
+      // each code byte is read once, RL lanes x 16 bytes per load (whole 128-byte lines when a row's
+      // H / 2 bytes are, as at H = 2560): the non-temporal hint (rotating experts, H = 2560: step 9.45 ->
+      // 8.9 us); not for the W2 read-ahead below, which is there to leave the W2 bytes in the cache
+      c[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(codes + 16 * g));
       sraw[i] = scales[mi];
       mraw[i] = group_meta2_raw<ML>(expert, L, mi);
     }
