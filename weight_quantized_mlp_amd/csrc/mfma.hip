@@ -633,7 +633,7 @@ __global__ void __launch_bounds__(256, 2) nv_gemm_kernel(int M, int K, int N, Nv
   const int rtail = nk % KSB;
   // FP8 weight blocks of a plan with one row of tiles are read by exactly one workgroup and are whole
   // 128-byte lines (128 code bytes per column, rows a multiple of 128 bytes when K is): those copies carry
-  // the non-temporal hint (FP8, M = 8: 70.0 -> 64.5 us per step).  NVFP4 blocks (144 bytes) share a line
+  // the non-temporal hint (FP8, M = 8: 69.9 -> 65.0 us per step).  NVFP4 blocks (144 bytes) share a line
   // with the next block of the column, which the hint would fetch twice (NVFP4, M = 8: 57.8 -> 62.6 us).
   const bool w_nt = FMT == 0 && BS && plan.ntm == 1 && (K & 127) == 0;
   auto copy_w = [&](int blk) {
