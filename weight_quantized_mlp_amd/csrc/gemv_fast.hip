@@ -212,14 +212,14 @@ __global__ void __launch_bounds__(64 * kRowWaves) nv_gu_grp(int M, int K, int N,
   // the workgroup barrier then waits only for x, not for every wave's weights.
   StageRegs<uint16_t, kRowStageRegs> sr;
   if constexpr (ONE) sr.issue(x, G);
-  u32x3 wv[2][CH];   // record bytes [8q, 8q+12): .x the scale dword (q = 0), .y .z the group's nibbles
+  u32x3_a4 wv[2][CH];   // record bytes [8q, 8q+12): .x the scale dword (q = 0), .y .z the group's nibbles
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
     const int g = min(lane + 64 * c, G - 1);   // clamped: in bounds, never accumulated
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       const uint8_t* p = (mt ? bu : bg) + (size_t)rl * rb + (size_t)(g >> 2) * 36 + 8 * (g & 3);
-      wv[mt][c] = __builtin_nontemporal_load(reinterpret_cast<const u32x3*>(__builtin_assume_aligned(p, 8)));
+      wv[mt][c] = __builtin_nontemporal_load(reinterpret_cast<const u32x3_a4*>(p));   // 4-byte aligned
     }
   }
   const int Mloop = ONE ? 1 : M;
