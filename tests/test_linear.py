@@ -68,12 +68,15 @@ def test_auto_tail_case_is_the_gemm():
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
 
 
+@pytest.mark.parametrize("K", [320, 512])
 @pytest.mark.parametrize("rows", [5, 37])
 @pytest.mark.parametrize("fmt", ["fp8", "nvfp4"])
-def test_short_batch_ragged_n_split_k(fmt, rows):
+def test_short_batch_ragged_n_split_k(fmt, rows, K):
     # A batch inside one tile row (32- or 64-row tile) with N = 67: one column tile, so the K range is
     # split and the finish launches workgroups for the batch's rows only and stores column by column.
-    N, K = 67, 320
+    # K = 512 (whole 128-byte FP8 rows, one row of 32-row tiles at 5 rows): the FP8 weight copies take
+    # the non-temporal hint.
+    N = 67
     x = x_rows(17 + rows, K)[:rows]
     if fmt == "fp8":
         r = np.random.default_rng(19)
