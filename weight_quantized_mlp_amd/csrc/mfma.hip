@@ -632,10 +632,12 @@ __global__ void __launch_bounds__(256, 2) nv_gemm_kernel(int M, int K, int N, Nv
   // window starts inside the row) and read_block moves those steps down to positions 0 .. r-1.
   const int rtail = nk % KSB;
   // FP8 weight blocks of a plan with one row of tiles are read by exactly one workgroup and are whole
-  // 128-byte lines (128 code bytes per column, rows a multiple of 128 bytes when K is): those copies carry
-  // the non-temporal hint (FP8, M = 8: 69.9 -> 65.0 us per step).  NVFP4 blocks (144 bytes) share a line
-  // with the next block of the column, which the hint would fetch twice (NVFP4, M = 8: 57.8 -> 62.6 us).
-  const bool w_nt = FMT == 0 && BS && plan.ntm == 1 && (K & 127) == 0;
+  // 128-byte lines (128 code bytes per column; rows start on a line when K and the matrix base are
+  // multiples of 128 bytes): those copies carry the non-temporal hint (FP8, M = 8: 69.9 -> 65.0 us per
+  // step).  NVFP4 blocks (144 bytes) share a line with the next block of the column, which the hint would
+  // fetch twice (NVFP4, M = 8: 57.8 -> 62.6 us).
+  const bool w_nt = FMT == 0 && BS && plan.ntm == 1 && (K & 127) == 0 && (((uintptr_t)w0 & 127) == 0) &&
+                    (!GU || ((uintptr_t)w1 & 127) == 0);
   auto copy_w = [&](int blk) {
     blk = min(blk, nblk - 1);
     const uint32_t boff = (rtail && blk == nblk - 1) ? rb - (uint32_t)CB : (uint32_t)blk * CB;
